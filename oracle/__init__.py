@@ -1,0 +1,18 @@
+"""fp64 CPU oracle for the fused low-rank MoE router -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP product path never imports,
+calls or links anything here.
+
+Method: "MoRE: Scaling mixture of experts with hardware-aware low-rank routing",
+§2 (standard and low-rank router), App. F eq. (5) (logits), App. F.1
+Algorithm 1 and Fig. 12 (exact top-k, softmax over the k selected logits),
+App. F.2.1 eq. (6) (full softmax / log-sum-exp).  The arithmetic lives in
+``more_oracle.c`` (plain C, fp64, OpenMP over tokens); this module only builds
+it with gcc and marshals numpy arrays through ctypes.
+"""
+from .oracle import (DT_BF16, DT_F32, DT_F64, GATE_FULL, GATE_TOPK, build, library_path,
+                     logits, max_threads, route_fullrank, route_lowrank)
+
+__all__ = ["DT_BF16", "DT_F32", "DT_F64", "GATE_FULL", "GATE_TOPK", "build", "library_path",
+           "logits", "max_threads", "route_fullrank", "route_lowrank"]

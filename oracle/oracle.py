@@ -1,0 +1,138 @@
+"""ctypes marshalling for the C oracle (TEST INFRASTRUCTURE; see package docstring)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+DT_BF16, DT_F32, DT_F64 = 0, 1, 2
+GATE_TOPK, GATE_FULL = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "more_oracle.c")
+_LIB = os.path.join(_HERE, "libmore_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_ERRORS = {1: "bad argument", 2: "non-finite input", 3: "out of memory"}
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP).  Plain C, no GPU code."""
+    global _lib
+    with _lock:
+        if force or not os.path.exists(_LIB):
+            tmp = _LIB + ".tmp%d" % os.getpid()
+            subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                                   "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+            os.replace(tmp, _LIB)
+            _lib = None
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = C.CDLL(_LIB)
+        p, i64, i32 = C.c_void_p, C.c_int64, C.c_int
+        lib.oracle_route_lowrank.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, i32,
+                                             p, p, p, p, p, p, p, i32]
+        lib.oracle_route_fullrank.argtypes = [i32, p, i64, i64, p, i64, p, i32, i32,
+                                              p, p, p, p, p, p, p, i32]
+        lib.oracle_logits.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, p]
+        for f in (lib.oracle_route_lowrank, lib.oracle_route_fullrank, lib.oracle_logits):
+            f.restype = C.c_int
+        lib.oracle_max_threads.restype = C.c_int
+        _lib = lib
+    return _lib
+
+
+def _dt_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return DT_BF16
+    if a.dtype == np.float32:
+        return DT_F32
+    if a.dtype == np.float64:
+        return DT_F64
+    raise TypeError(f"unsupported storage dtype {a.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise RuntimeError(f"oracle error {rc}: {_ERRORS.get(rc, 'unknown')}")
+
+
+def _outputs(N: int, k: int):
+    return dict(idx=np.empty((N, k), np.int32), gate=np.empty((N, k), np.float64),
+                logit=np.empty((N, k), np.float64), lse=np.empty(N, np.float64),
+                kth=np.empty(N, np.float64), kp1=np.empty(N, np.float64),
+                maxabs=np.empty(N, np.float64))
+
+
+def route_lowrank(X, R1, R2, bias, k: int, gate: int = GATE_TOPK, nthreads: int = 0) -> dict:
+    """Exact top-k of (x R1) R2 + b per token; returns idx, gate, logit, lse, kth, kp1, maxabs."""
+    X, R1, R2 = (np.ascontiguousarray(a) for a in (X, R1, R2))
+    dt = _dt_code(X)
+    assert _dt_code(R1) == dt and _dt_code(R2) == dt
+    N, h = X.shape
+    h2, r = R1.shape
+    r2, M = R2.shape
+    assert h2 == h and r2 == r
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = _outputs(N, k)
+    _check(_load().oracle_route_lowrank(dt, _ptr(X), N, h, _ptr(R1), r, _ptr(R2), M, _ptr(b), k, gate,
+                                        _ptr(out["idx"]), _ptr(out["gate"]), _ptr(out["logit"]),
+                                        _ptr(out["lse"]), _ptr(out["kth"]), _ptr(out["kp1"]),
+                                        _ptr(out["maxabs"]), nthreads))
+    return out
+
+
+def route_fullrank(X, W, bias, k: int, gate: int = GATE_TOPK, nthreads: int = 0) -> dict:
+    """Exact top-k of x W + b per token (the standard router of §2)."""
+    X, W = np.ascontiguousarray(X), np.ascontiguousarray(W)
+    dt = _dt_code(X)
+    assert _dt_code(W) == dt
+    N, h = X.shape
+    h2, M = W.shape
+    assert h2 == h
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = _outputs(N, k)
+    _check(_load().oracle_route_fullrank(dt, _ptr(X), N, h, _ptr(W), M, _ptr(b), k, gate,
+                                         _ptr(out["idx"]), _ptr(out["gate"]), _ptr(out["logit"]),
+                                         _ptr(out["lse"]), _ptr(out["kth"]), _ptr(out["kp1"]),
+                                         _ptr(out["maxabs"]), nthreads))
+    return out
+
+
+def logits(X, A, B, bias, fullrank: bool = False) -> np.ndarray:
+    """All N x M fp64 logits: (x A) B + b, or x A + b when fullrank (A = W)."""
+    X, A = np.ascontiguousarray(X), np.ascontiguousarray(A)
+    dt = _dt_code(X)
+    N, h = X.shape
+    if fullrank:
+        M, r = A.shape[1], 0
+    else:
+        B = np.ascontiguousarray(B)
+        r, M = B.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty((N, M), np.float64)
+    _check(_load().oracle_logits(dt, _ptr(X), N, h, _ptr(A), r, _ptr(None if fullrank else B), M,
+                                 _ptr(b), int(fullrank), _ptr(out)))
+    return out
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
