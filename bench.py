@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Routed tokens/s of the fused low-rank MoE router on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload headline]
+
+A step is one full routing call (more_route_lowrank: sweep-order/weight packing
+kernel + the fused router kernel) over one batch of synthetic tokens already
+resident in HBM.  Prints ONE JSON line:
+  value          routed tokens/s = N / mean step time
+  roofline       the fused router kernel alone, timed with HIP events on its
+                 stream: algorithmic bytes (X + outputs + weights) per launch
+                 over its mean duration, against the 8 TB/s HBM peak
+  pct_roofline   roofline time / step time, roofline time = max(X bytes / 8 TB/s,
+                 2N(hr + rM) / 2.5 PFLOP/s)
+  cpu_baseline   the fp64 oracle on a bounded sample of the same tokens, timed
+                 on the host cores (rank 0, one GPU only)
+  fullrank       the fused full-rank (standard) router on the same tokens
+  context        published B200 figures of the paper (other hardware)
+Only one GPU is supported: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published (no sparsity)
+CONTEXT = {
+    "source": "MoRE: Scaling mixture of experts with hardware-aware low-rank routing (B200, bf16)",
+    "note": "other hardware and other shapes; no figure is published at this workload",
+    "router_alone_ms_EPa_h512_r64_k4_N262144": {"M2048": 1.68, "M8192": 6.09, "M16384": 11.95,
+                                                "table": "Table 10(a)"},
+    "standard_router_ms_same_setting": {"M2048": 8.20, "M8192": 27.90, "M16384": 45.30},
+    "fused_vs_unfused_lowrank_speedup_h2048_M4096_r16_k4": {"B2": 1.4, "B256": 6.3, "figure": "Fig. 24"},
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-fullrank", action="store_true")
+    ap.add_argument("--fullrank-steps", type=int, default=3)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(cfg, k, with_lse):
+    x = cfg.N * cfg.h * 2
+    out = cfg.N * k * 8 + (cfg.N * 4 if with_lse else 0)
+    if cfg.fullrank:
+        w = cfg.h * cfg.M * 2
+    else:
+        w = (cfg.h * cfg.r + cfg.r * cfg.M) * 2
+    w += cfg.M * 4 if cfg.has_bias else 0
+    return x + out + w
+
+
+def roofline_time_s(cfg):
+    return max(cfg.x_bytes() / (HBM_PEAK_GBS * 1e9), cfg.flops() / (BF16_PEAK_TFLOPS * 1e12))
+
+
+def time_events(torch, fn, steps, stream):
+    """Mean ms of fn() over `steps` launches, each bracketed by its own events on `stream`."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for s, e in ev:
+            s.record(stream)
+            fn()
+            e.record(stream)
+    stream.synchronize()
+    ms = sorted(s.elapsed_time(e) for s, e in ev)
+    return sum(ms) / len(ms), ms[len(ms) // 2], ms[len(ms) // 10], ms[(9 * len(ms)) // 10]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this router benchmark runs on exactly one GPU; "
+                                   "multi-GPU runs are not supported (token sharding would need no "
+                                   "communication, so one GPU's share is the measured kernel)"}))
+        return 2
+    import numpy as np
+    import torch
+
+    from rank_router_top_amd import configs as CF
+    from rank_router_top_amd import route as R
+
+    cfg = CF.ALL[args.workload]
+    assert not cfg.fullrank
+    gate = cfg.gates[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    t0 = time.time()
+    log(f"generating {cfg.name}: N={cfg.N} h={cfg.h} M={cfg.M} r={cfg.r} k={cfg.k}")
+    X_np = cfg.x_rows(args.seed)
+    R1_np, R2_np, b_np = cfg.weights(args.seed)
+    X = R.to_device(X_np, dev)
+    R1, R2, b = (R.to_device(a, dev) for a in (R1_np, R2_np, b_np))
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    dt = R.MORE_DT_BF16
+    nb = R.workspace_bytes(False, dt, cfg.N, cfg.h, cfg.r, cfg.M, cfg.k, gate, b is not None)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    out = dict(idx=torch.empty((cfg.N, cfg.k), dtype=torch.int32, device=dev),
+               gate=torch.empty((cfg.N, cfg.k), dtype=torch.float32, device=dev),
+               logit=None, lse=None)
+
+    def step():
+        R.route_lowrank(X, R1, R2, b, cfg.k, gate, out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_step = (t_end - t_start) * 1e3 / args.steps
+    log(f"step {ms_step:.4f} ms")
+
+    # the fused router kernel alone (weights packed once, as for static weights)
+    R.pack_lowrank(R1, R2, b, ws, stream=stream)
+
+    def kernel_only():
+        R.route_lowrank_packed(X, cfg.r, cfg.M, cfg.k, gate, ws, out=out, stream=stream)
+
+    for _ in range(3):
+        kernel_only()
+    k_mean, k_med, k_p10, k_p90 = time_events(torch, kernel_only, max(args.steps, 20), stream)
+
+    def pack_only():
+        R.pack_lowrank(R1, R2, b, ws, stream=stream)
+
+    p_mean = time_events(torch, pack_only, 20, stream)[0]
+    log(f"router kernel mean {k_mean:.4f} ms (p10 {k_p10:.4f}, p90 {k_p90:.4f}); pack {p_mean:.4f} ms")
+
+    alg_bytes = algorithmic_bytes(cfg, cfg.k, False)
+    achieved = alg_bytes / (k_mean * 1e-3) / 1e9
+    rt = roofline_time_s(cfg)
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
+    if os.path.exists(tpath):
+        try:
+            tr = json.load(open(tpath))
+            traffic = tr.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    result = {
+        "metric": "routed tokens/sec & % roofline, N=262144 h=2048 M=4096 r=32 k=8, 1 GPU",
+        "value": cfg.N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy: RMS-normalised Gaussian tokens, Gaussian weights, N(0,0.5) bias)",
+        "config": {"workload": cfg.name, "N": cfg.N, "h": cfg.h, "M": cfg.M, "r": cfg.r, "k": cfg.k,
+                   "gate": "topk_softmax" if gate == 0 else "full_softmax", "bias": cfg.has_bias,
+                   "parallelism": "single GPU"},
+        "pct_roofline": rt / (ms_step * 1e-3),
+        "roofline_time_us": rt * 1e6,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "lowrank_kernel", "kernel_ms": k_mean, "kernel_ms_median": k_med,
+                     "kernel_ms_p10": k_p10, "kernel_ms_p90": k_p90,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "mfma_tflops": cfg.flops() / (k_mean * 1e-3) / 1e12,
+                     "pack_kernel_ms": p_mean},
+        "context": CONTEXT,
+    }
+
+    if not args.no_fullrank:
+        FR = CF.FULLRANK
+        n_fr = cfg.N
+        W_np, _, bw_np = FR.weights(args.seed)
+        W, bw = R.to_device(W_np, dev), R.to_device(bw_np, dev)
+        nbw = R.workspace_bytes(True, dt, n_fr, FR.h, 0, FR.M, FR.k, 0, True)
+        wsw = torch.empty(nbw, dtype=torch.uint8, device=dev)
+
+        def fr_step():
+            R.route_fullrank(X, W, bw, FR.k, 0, out=out, workspace=wsw, stream=stream)
+
+        fr_step()
+        torch.cuda.synchronize()
+        fr_ms = time_events(torch, fr_step, args.fullrank_steps, stream)[0]
+        fr_roof = max(FR.x_bytes() / (HBM_PEAK_GBS * 1e9), FR.flops() / (BF16_PEAK_TFLOPS * 1e12))
+        result["fullrank"] = {"value": n_fr / (fr_ms * 1e-3), "unit": "tokens/s", "ms_per_step": fr_ms,
+                              "pct_roofline": fr_roof / (fr_ms * 1e-3), "bound": "mfma",
+                              "tflops": FR.flops() / (fr_ms * 1e-3) / 1e12, "peak_tflops": BF16_PEAK_TFLOPS}
+        log(f"fullrank {fr_ms:.3f} ms")
+        del W, wsw
+
+    if not args.no_cpu:
+        import oracle
+        oracle.build(force=False)
+        threads = oracle.max_threads()
+        n0 = 1024
+        t = time.perf_counter()
+        oracle.route_lowrank(X_np[:n0], R1_np, R2_np, b_np, cfg.k, gate, nthreads=threads)
+        per_tok = (time.perf_counter() - t) / n0
+        n = int(min(cfg.N, max(n0, args.cpu_seconds / max(per_tok, 1e-9))))
+        t = time.perf_counter()
+        oracle.route_lowrank(X_np[:n], R1_np, R2_np, b_np, cfg.k, gate, nthreads=threads)
+        dt_cpu = time.perf_counter() - t
+        result["cpu_baseline"] = {"value": n / dt_cpu, "unit": "tokens/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"first {n} of the {cfg.N} tokens, same weights, fp64, "
+                                            f"{dt_cpu:.1f} s wall"}
+        log(f"cpu oracle {n / dt_cpu:.0f} tokens/s on {threads} threads")
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

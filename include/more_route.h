@@ -1,0 +1,166 @@
+/*
+ * more_route.h -- C ABI of the MI355X (gfx950) fused MoE router library
+ * (libmore_route.so).
+ *
+ * Method: "MoRE: Scaling mixture of experts with hardware-aware low-rank
+ * routing" (Wong, Goel, Boix-Adsera).
+ *   - §2: the standard router g(x) = softmax(TopK(R x)) and the low-rank
+ *     router, where R is replaced by the product of a rank-r down-projection
+ *     and an up-projection.
+ *   - App. F, eq. (5): logits of all tokens and experts; App. F.1,
+ *     Algorithm 1: one fused pass that never writes the N x M logits and
+ *     returns the top-k values and indices; Fig. 12: gate weights are a
+ *     softmax over the k selected logits.
+ *   - App. F.2.1, eq. (6) and eq. (8): the full softmax over all M experts,
+ *     built with a running maximum and a running normaliser across expert
+ *     tiles (online log-sum-exp).
+ *
+ * Convention.  R1 is the h x r down-projection and R2 the r x M
+ * up-projection, both row-major, so token x (a row of X) has logits
+ * l = (x R1) R2 + b.  (The paper writes the factors the other way round:
+ * its down-projection is our R1 transposed and its up-projection our R2
+ * transposed.)  The full-rank router takes W (h x M, row-major): l = x W + b.
+ *
+ * Common rules for every routing call:
+ *   Pointers.  X, R1, R2, W, bias and every output are DEVICE pointers
+ *   (hipMalloc'd or torch CUDA tensors) on the current HIP device.  All
+ *   tensors are dense row-major and 16-byte aligned.  Ownership stays with
+ *   the caller; the library allocates and frees nothing and keeps no state
+ *   between calls, so calls on different streams may run concurrently as long
+ *   as their outputs and workspaces do not overlap.
+ *   Asynchrony.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *   legacy default stream) and the call returns without synchronising.
+ *   Outputs are valid once the stream reaches that point.
+ *   Errors.  Arguments are validated on the host before any HIP call; a
+ *   failed check returns its code and enqueues nothing.  MORE_ERR_HIP means a
+ *   kernel launch was rejected; faults during execution surface at the
+ *   caller's next synchronisation, not here.
+ *   Contract.  1 <= k <= min(M, 32); N >= 0 (N = 0 is a no-op); h, M >= 1;
+ *   h % 8 == 0; for the low-rank router r % 16 == 0 and r <= 128.  Inputs
+ *   must be finite: non-finite inputs give undefined results.
+ *   Outputs.  Per token the k experts are listed by logit descending; equal
+ *   logits are listed by expert index ascending, and when equal logits
+ *   straddle the k-th place the lower indices are selected.  topk_idx is
+ *   int32 (N x k); topk_gate, topk_logit (N x k) and lse (N) are fp32.  The
+ *   logits are computed with fp32 accumulation of exact bf16 (or fp32)
+ *   products; the down-projection result enters the second product as a
+ *   bf16 hi+lo pair, i.e. at about 16 significant bits.
+ *   Gates.  MORE_GATE_TOPK_SOFTMAX: g_j = exp(l_j - l_1) / sum over the k
+ *   selected of exp(l_i - l_1).  MORE_GATE_FULL_SOFTMAX: g_j = exp(l_j - lse)
+ *   with lse = log sum over all M experts of exp(l) (not renormalised).
+ *   Workspace.  Device scratch owned by the caller, at least
+ *   more_route_workspace_bytes(...) bytes for the same arguments, 256-byte
+ *   aligned.  It carries the per-call packed weights and, for small token
+ *   counts, partial results.  Its contents need no initialisation and are
+ *   garbage afterwards.  Two calls in flight must not share a workspace.
+ */
+#ifndef MORE_ROUTE_H
+#define MORE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MORE_ABI_VERSION 1
+#define MORE_MAX_K 32
+#define MORE_MAX_R 128
+
+typedef enum {
+    MORE_OK = 0,
+    MORE_ERR_NULL_ARG = 1,    /* a required pointer is NULL                      */
+    MORE_ERR_BAD_SHAPE = 2,   /* N < 0, h < 1, M < 1, r < 1, or size overflow    */
+    MORE_ERR_BAD_K = 3,       /* k < 1, k > M or k > MORE_MAX_K                 */
+    MORE_ERR_BAD_DTYPE = 4,   /* unknown more_dtype                              */
+    MORE_ERR_BAD_GATE = 5,    /* unknown more_gate                               */
+    MORE_ERR_WORKSPACE = 6,   /* workspace NULL/too small/misaligned             */
+    MORE_ERR_UNSUPPORTED = 7, /* outside the envelope: h % 8, r % 16, r > 128    */
+    MORE_ERR_HIP = 8,         /* a HIP launch or query failed                    */
+    MORE_ERR_ALIGNMENT = 9    /* a tensor pointer is not 16-byte aligned         */
+} more_status;
+
+typedef enum {
+    MORE_DT_BF16 = 0, /* X, R1, R2 (or W) stored as bf16 */
+    MORE_DT_F32 = 1   /* X, R1, R2 (or W) stored as fp32 */
+} more_dtype;
+
+typedef enum {
+    MORE_GATE_TOPK_SOFTMAX = 0, /* softmax over the k selected logits (Fig. 12)      */
+    MORE_GATE_FULL_SOFTMAX = 1  /* full-softmax probability via online LSE (eq. 6/8) */
+} more_gate;
+
+/*
+ * Fused low-rank router + top-k + gates (App. F.1 Algorithm 1; gates per
+ * Fig. 12 or eq. (6)).  One pass over X: z = x R1 stays on chip, the experts
+ * are swept in tiles of z R2 + b with a streaming top-k, and only the
+ * N x k results reach memory.
+ *   dt          storage type of X, R1 and R2.
+ *   X           N x h.          R1  h x r.          R2  r x M.
+ *   bias        M fp32, or NULL for no bias.  The biased logit drives both
+ *               selection and gates.
+ *   k, gate     as above.
+ *   topk_idx    N x k int32 (required).   topk_gate  N x k fp32 (required).
+ *   topk_logit  N x k fp32 or NULL.       lse        N fp32 or NULL; written
+ *               only in FULL_SOFTMAX mode.
+ *   workspace   see above; size from more_route_workspace_bytes(0, ...).
+ *   stream      hipStream_t or NULL.
+ */
+more_status more_route_lowrank(more_dtype dt, const void* X, int64_t N, int64_t h, const void* R1,
+                               int64_t r, const void* R2, int64_t M, const float* bias, int32_t k,
+                               more_gate gate, int32_t* topk_idx, float* topk_gate,
+                               float* topk_logit, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Split form of more_route_lowrank for static weights: more_lowrank_pack
+ * writes the sweep order and the MFMA-ordered copies of R1, R2 and the bias
+ * into `workspace` (size from more_route_workspace_bytes(0, ...)); after it,
+ * more_lowrank_route_packed routes any number of token batches against that
+ * workspace without touching R1, R2 or the bias again.  The two calls must
+ * agree on dt, h, r and M (and on whether a bias was given); the library
+ * cannot check this because the packed data lives on the device.
+ * more_route_lowrank(...) is exactly more_lowrank_pack followed by
+ * more_lowrank_route_packed on the same stream.
+ */
+more_status more_lowrank_pack(more_dtype dt, const void* R1, int64_t h, int64_t r, const void* R2,
+                              int64_t M, const float* bias, void* workspace, size_t workspace_bytes,
+                              void* stream);
+more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int64_t r,
+                                      int64_t M, int32_t k, more_gate gate, int32_t* topk_idx,
+                                      float* topk_gate, float* topk_logit, float* lse,
+                                      const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused standard (full-rank) router + top-k + gates: the same selection and
+ * gates with l = x W + b (§2 standard router; App. H.3 Fig. 20 fuses it the
+ * same way, reloading weight tiles instead of a rank-r intermediate).
+ *   W  h x M.  Other arguments as for more_route_lowrank.
+ *   workspace  size from more_route_workspace_bytes(1, ...).
+ */
+more_status more_route_fullrank(more_dtype dt, const void* X, int64_t N, int64_t h, const void* W,
+                                int64_t M, const float* bias, int32_t k, more_gate gate,
+                                int32_t* topk_idx, float* topk_gate, float* topk_logit, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes needed by a routing call with these arguments (fullrank = 0
+ * for more_route_lowrank, 1 for more_route_fullrank; r is ignored for full
+ * rank; has_bias != 0 when a bias pointer will be passed).  Returns 0 for
+ * arguments the call would reject.  Pure host function, no HIP call.
+ */
+size_t more_route_workspace_bytes(int fullrank, more_dtype dt, int64_t N, int64_t h, int64_t r,
+                                  int64_t M, int32_t k, more_gate gate, int has_bias);
+
+/* Static string for a status code (never NULL). */
+const char* more_status_str(more_status s);
+
+/* MORE_ABI_VERSION of the built library. */
+int more_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MORE_ROUTE_H */

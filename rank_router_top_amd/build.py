@@ -1,0 +1,82 @@
+"""Build libmore_route.so (HIP, gfx950) in-tree.
+
+    python -m rank_router_top_amd.build            # compile every unit, then link
+    python -m rank_router_top_amd.build --jobs 4
+
+Each ``csrc/*.hip`` unit is compiled separately (in parallel) with hipcc for
+gfx950 only and linked into ``rank_router_top_amd/libmore_route.so``.  Packed
+fp32 VALU instructions are disabled on the device side (the host pass prints a
+harmless "not a recognized feature" warning for that flag).
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libmore_route.so")
+ARCH = "gfx950"
+
+CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wall", "-Wno-unused-function"]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libmore_route.so")
+    return exe
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
+    cmd = [hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    noise = "-packed-fp32-ops' is not a recognized feature"
+    out = "\n".join(l for l in res.stdout.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{out}")
+    if out.strip() and verbose:
+        print(out)
+    return obj
+
+
+def build(jobs: int = 0, verbose: bool = False) -> str:
+    """Compile all units and link the shared library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = jobs or min(len(srcs), os.cpu_count() or 1, 8)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--jobs", type=int, default=0)
+    ap.add_argument("-v", "--verbose", action="store_true")
+    args = ap.parse_args(argv)
+    print(build(args.jobs, args.verbose))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

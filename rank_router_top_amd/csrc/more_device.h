@@ -1,0 +1,193 @@
+// more_device.h -- device-side building blocks shared by the MI355X router kernels.
+//
+// Method: "MoRE: Scaling mixture of experts with hardware-aware low-rank
+// routing", App. F.1 Algorithm 1 (single sweep over the experts with a running
+// top-k buffer) and App. F.2.1 eq. (8) (running maximum / normaliser).
+//
+// CDNA4 mapping used throughout:
+//  * Logit tiles come out of a 32x32 MFMA in transposed form: rows are 32
+//    experts, columns are 32 tokens.  Lane l (half hf = l/32) owns token l%32
+//    and the 16 accumulator rows 8q + 4hf + e (q, e in 0..3), i.e. acc[4q+e].
+//    So each token is shared by two lanes, each seeing half of the experts.
+//  * Each lane keeps the k best VALUES it has seen as a descending register
+//    list updated with v_med3 (k VALU ops per insert, no index bookkeeping),
+//    and appends every accepted (value, sweep position) pair to a per-lane
+//    log in LDS.  The indices are recovered from the log once at the end.
+//  * A candidate must reach the effective threshold max(own k-th, partner's
+//    k-th): both are lower bounds of the token's final k-th logit.  Equality
+//    is accepted (>=) so that exact ties are resolved at the end by expert
+//    index, whatever order the experts were swept in.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace more {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+
+constexpr int kWave = 64;
+constexpr int kTile = 32;                // experts per tile == tokens per wave
+constexpr float kLowest = -3.4028234663852886e38f;   // -FLT_MAX: start of every list
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ floatx16 mfma_bf16(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma_f32(float a, float b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Value held by lane l^32 (the other half of the same token column).
+__device__ __forceinline__ uint32_t partner_u32(uint32_t x, bool hi_half) {
+  auto pr = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return hi_half ? pr[0] : pr[1];
+}
+__device__ __forceinline__ float partner_f32(float x, bool hi_half) {
+  return __uint_as_float(partner_u32(__float_as_uint(x), hi_half));
+}
+
+__device__ __forceinline__ bool any_lane(bool c) {
+  return __builtin_amdgcn_ballot_w64(c) != 0;
+}
+
+// Log entry: (logit, sweep position) packed in a float2 (position as raw bits).
+struct LogRef {
+  float2* base;   // this wave's log: entry c of lane l at base[c * 64 + l]
+};
+
+template <int KMAX, int CAP>
+struct SweepState {
+  float L[KMAX];   // descending; the first KMAX-k slots hold +inf (runtime k < KMAX)
+  float thr_p;     // partner's k-th (possibly stale: still a valid lower bound)
+  float thr;       // max(L[KMAX-1], thr_p)
+  int cnt;         // log entries of this lane
+  float m, Z;      // running max / normaliser (full-softmax gate only)
+
+  __device__ __forceinline__ void init(int k) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) L[j] = (j < KMAX - k) ? __builtin_inff() : kLowest;
+    thr_p = kLowest;
+    thr = kLowest;
+    cnt = 0;
+    m = kLowest * 0.25f;
+    Z = 0.f;
+  }
+
+  // Insert value x at sweep position pos (lanes masked by the caller).
+  __device__ __forceinline__ void insert(float x, int pos, LogRef lg, int lane) {
+#pragma unroll
+    for (int j = KMAX - 1; j >= 1; --j) L[j] = __builtin_amdgcn_fmed3f(L[j - 1], L[j], x);
+    L[0] = fmaxf(L[0], x);
+    lg.base[cnt * kWave + lane] = make_float2(x, __int_as_float(pos));
+    ++cnt;
+    thr = fmaxf(L[KMAX - 1], thr_p);
+  }
+
+  // Drop log entries that can no longer reach the top-k (value < thr).  When
+  // exact ties at thr keep the log full, keep only the k ties of lowest expert
+  // index (the tie rule); entries of higher rank among the ties can never be
+  // selected.  Called with the whole wave active.
+  __device__ void compact(LogRef lg, int lane, const int* __restrict__ perm, int k) {
+    int w = 0;
+    for (int c = 0; c < CAP; ++c) {
+      if (c < cnt) {
+        float2 e = lg.base[c * kWave + lane];
+        if (e.x >= thr) {
+          lg.base[w * kWave + lane] = e;
+          ++w;
+        }
+      }
+    }
+    cnt = w;
+    if (any_lane(cnt > CAP - 8)) {
+      if (cnt > CAP - 8) {
+        // pass 1: knock out ties of rank >= k (rank by original expert index)
+        for (int c = 0; c < cnt; ++c) {
+          float2 e = lg.base[c * kWave + lane];
+          if (e.x == thr) {
+            const int oi = perm[__float_as_int(e.y)];
+            int rank = 0;
+            for (int c2 = 0; c2 < cnt; ++c2) {
+              float2 e2 = lg.base[c2 * kWave + lane];
+              if (e2.x == thr && perm[__float_as_int(e2.y)] < oi) ++rank;
+            }
+            if (rank >= k) lg.base[c * kWave + lane] = make_float2(-__builtin_inff(), e.y);
+          }
+        }
+        // pass 2: squeeze out the knocked-out entries
+        w = 0;
+        for (int c = 0; c < cnt; ++c) {
+          float2 e = lg.base[c * kWave + lane];
+          if (e.x >= thr) {
+            lg.base[w * kWave + lane] = e;
+            ++w;
+          }
+        }
+        cnt = w;
+      }
+    }
+  }
+
+  // One 32-expert tile: acc holds this lane's 16 logits (bias included,
+  // -inf on padding rows); pos_base = 32*t + 4*hf.
+  template <bool FULL>
+  __device__ __forceinline__ void tile(const floatx16& acc, int pos_base, LogRef lg, int lane,
+                                       bool hi_half, const int* __restrict__ perm, int k) {
+    float g[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      g[q] = fmaxf(fmaxf(acc[4 * q], acc[4 * q + 1]), fmaxf(acc[4 * q + 2], acc[4 * q + 3]));
+    const float tmax = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
+    if (FULL) {
+      // eq. (8): rescale the running sum when the maximum moves, then add the tile.
+      const float mn = fmaxf(m, tmax);
+      const float mb = mn * kLog2e;
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kLog2e, -mb));
+      Z = Z * __builtin_amdgcn_exp2f((m - mn) * kLog2e) + s;
+      m = mn;
+    }
+    thr_p = partner_f32(L[KMAX - 1], hi_half);
+    thr = fmaxf(L[KMAX - 1], thr_p);
+    if (any_lane(tmax >= thr)) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (any_lane(g[q] >= thr)) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = acc[4 * q + e];
+            if (x >= thr) insert(x, pos_base + 8 * q + e, lg, lane);
+          }
+          if (any_lane(cnt > CAP - 4)) compact(lg, lane, perm, k);
+        }
+      }
+    }
+  }
+};
+
+// Tie-aware sorted insertion used once per token at the end: order is
+// (value descending, original expert index ascending).
+template <int KMAX>
+__device__ __forceinline__ void ordered_insert(float (&V)[KMAX], int (&IX)[KMAX], float x, int ix) {
+  bool c[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) c[j] = (x > V[j]) || (x == V[j] && ix < IX[j]);
+#pragma unroll
+  for (int j = KMAX - 1; j >= 1; --j) {
+    const float nv = c[j - 1] ? V[j - 1] : (c[j] ? x : V[j]);
+    const int ni = c[j - 1] ? IX[j - 1] : (c[j] ? ix : IX[j]);
+    V[j] = nv;
+    IX[j] = ni;
+  }
+  if (c[0]) {
+    V[0] = x;
+    IX[0] = ix;
+  }
+}
+
+}  // namespace more

@@ -1,0 +1,42 @@
+// more_dispatch.h -- kernel selection across the compile units that hold the
+// template instances (split so the library builds in parallel).
+#pragma once
+#include "more_lowrank.h"
+#include "more_fullrank.h"
+
+namespace more {
+
+typedef void (*lowrank_fn)(LowRankArgs);
+typedef void (*fullrank_fn)(FullRankArgs);
+
+// Waves per workgroup: each wave's log takes (2*KMAX+8)*512 bytes of LDS;
+// keep a workgroup within 64 KiB.
+constexpr int waves_for_kmax(int kmax) { return kmax <= 8 ? 4 : (kmax == 16 ? 2 : 1); }
+
+lowrank_fn pick_lowrank_bf16_topk(int kmax, int r16);
+lowrank_fn pick_lowrank_bf16_full(int kmax, int r16);
+lowrank_fn pick_lowrank_f32(bool full, int kmax, int r16);
+fullrank_fn pick_fullrank(int dt, bool full, int kmax);
+
+template <int DT, int KMAX, bool FULL>
+lowrank_fn pick_lowrank_r(int r16) {
+  constexpr int W = waves_for_kmax(KMAX);
+  switch (r16) {
+    case 1: return lowrank_kernel<DT, KMAX, FULL, 1, W>;
+    case 2: return lowrank_kernel<DT, KMAX, FULL, 2, W>;
+    case 4: return lowrank_kernel<DT, KMAX, FULL, 4, W>;
+    default: return lowrank_kernel<DT, KMAX, FULL, 8, W>;
+  }
+}
+
+template <int DT, bool FULL>
+lowrank_fn pick_lowrank_k(int kmax, int r16) {
+  switch (kmax) {
+    case 4: return pick_lowrank_r<DT, 4, FULL>(r16);
+    case 8: return pick_lowrank_r<DT, 8, FULL>(r16);
+    case 16: return pick_lowrank_r<DT, 16, FULL>(r16);
+    default: return pick_lowrank_r<DT, 32, FULL>(r16);
+  }
+}
+
+}  // namespace more

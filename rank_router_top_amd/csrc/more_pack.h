@@ -1,0 +1,129 @@
+// more_pack.h -- per-call preparation: expert sweep order and MFMA operand packing.
+//
+// The fused kernels read every weight operand with one 16-byte load per lane
+// in the exact register layout the MFMA wants, from a packed copy in the
+// caller's workspace (L2-resident: 128 KiB + 256 KiB at h=2048, r=32, M=4096).
+//
+// Sweep order.  Without a bias the experts are swept in index order.  With a
+// bias they are swept by bias descending (ties by index): experts with a large
+// bias tend to end in the top-k, so the running k-th value rises early and
+// fewer later logits pass the filter.  The selected set and its order do not
+// depend on the sweep order (ties are resolved by expert index at the end),
+// so this is purely a speed choice.
+#pragma once
+#include "more_device.h"
+
+namespace more {
+
+// Position p of the sweep holds expert perm[p] (perm[p] = -1 on the padding
+// positions M..M_pad-1).  Row i of tile t is position 32t + i.  For a lane of
+// half hf, accumulator register v holds row 8*(v>>2) + 4*hf + (v&3).
+__host__ __device__ inline int acc_row(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
+
+struct PackArgs {
+  // inputs
+  const void* R1;     // h x r (bf16 bits or fp32)
+  const void* R2;     // r x M, or W (h x M) for full rank
+  const float* bias;  // M or null
+  int h, r, M, Mpad, NT;
+  int kdim;           // contraction length of the second product: r (low rank) or h (full rank)
+  int ksteps2;        // MFMA K-steps of the second product
+  int ksteps1, rb;    // first product: K-steps over h and 32-row blocks of z (low rank only)
+  int natural_k;      // 1: second-product K rows in memory order (full rank: the X operand)
+  int rank_blocks;    // blocks computing the sweep order (64 experts each)
+  int r1_blocks;      // blocks packing R1
+  // outputs (workspace)
+  void* R1p;
+  void* R2p;
+  float* biasp;       // [NT][2][16]
+  int* perm;          // [Mpad]
+};
+
+// Element type helpers.
+template <int DT> struct Elem;
+template <> struct Elem<0> { typedef uint16_t T; };   // bf16 bits
+template <> struct Elem<1> { typedef float T; };
+
+// K index (row of R2 / W) carried by element e of K-step m for lane half hf.
+// Low rank (natural = 0), the rows of z as the first product left them:
+//  bf16 (8 elements per lane): rho = 16m + 8(e>>2) + 4hf + (e&3), which is
+//    accumulator register v = 8*(m&1) + e of 32-row block m>>1, so z feeds
+//    the second MFMA without any shuffle.
+//  fp32 (1 element per lane, K=2): rho = 32(m>>4) + acc_row(m & 15, hf).
+// Full rank (natural = 1), the memory order of an X row, which each lane loads
+// as consecutive elements: 16m + 8hf + e (bf16) or 2m + hf (fp32).
+template <int DT>
+__host__ __device__ inline int k_row(int m, int e, int hf, int natural) {
+  if (natural) return (DT == 0) ? 16 * m + 8 * hf + e : 2 * m + hf;
+  if (DT == 0) return 16 * m + 8 * (e >> 2) + 4 * hf + (e & 3);
+  return 32 * (m >> 4) + acc_row(m & 15, hf);
+}
+
+template <int DT>
+__global__ __launch_bounds__(1024) void pack_kernel(PackArgs a) {
+  typedef typename Elem<DT>::T T;
+  constexpr int EPL = (DT == 0) ? 8 : 1;          // elements per lane per K-step
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < a.rank_blocks) {
+    // ---- sweep order: rank of expert j by (bias desc, index asc); padding last
+    __shared__ int part[16][64];
+    const int jl = tid & 63, slice = tid >> 6;   // 64 experts x 16 slices
+    const int j = blockIdx.x * 64 + jl;
+    int cnt = 0;
+    if (a.bias && j < a.M) {
+      const float bj = a.bias[j];
+      const int per = (a.M + 15) / 16;
+      const int i0 = slice * per, i1 = min(a.M, i0 + per);
+      for (int i = i0; i < i1; ++i) {
+        const float bi = a.bias[i];
+        cnt += (bi > bj) || (bi == bj && i < j);
+      }
+    }
+    part[slice][jl] = cnt;
+    __syncthreads();
+    if (j >= a.Mpad) return;
+    int pos;
+    if (a.bias && j < a.M) {
+      pos = 0;
+      for (int s = 0; s < 16; ++s) pos += part[s][jl];
+    } else {
+      pos = j;
+    }
+    const int t = pos >> 5, i = pos & 31;
+    const T* B = (const T*)a.R2;
+    T* Bp = (T*)a.R2p;
+    // scatter column j of R2 (or W) into the packed tile at row i
+    for (int w = slice; w < a.ksteps2 * 2 * EPL; w += 16) {
+      const int m = w / (2 * EPL), hf = (w / EPL) & 1, e = w % EPL;
+      const int kr = k_row<DT>(m, e, hf, a.natural_k);
+      T val = 0;
+      if (j < a.M && kr < a.kdim) val = B[(size_t)kr * a.M + j];
+      Bp[(((size_t)t * a.ksteps2 + m) * kWave + i + 32 * hf) * EPL + e] = val;
+    }
+    if (slice == 0) {
+      a.perm[pos] = (j < a.M) ? j : -1;
+      const int hf = (i >> 2) & 1, v = 4 * (i >> 3) + (i & 3);
+      a.biasp[(t * 2 + hf) * 16 + v] = (j < a.M) ? (a.bias ? a.bias[j] : 0.f) : -__builtin_inff();
+    }
+    return;
+  }
+  // ---- R1 packing (low rank only): entry (s, b, lane) holds the A operand of
+  // K-step s for 32-row block b of z.
+  const int gidx = ((int)blockIdx.x - a.rank_blocks) * 1024 + tid;
+  const int total = a.ksteps1 * a.rb * kWave;
+  if (gidx >= total) return;
+  const int lane = gidx % kWave, sb = gidx / kWave;
+  const int b = sb % a.rb, s = sb / a.rb;
+  const int hf = lane >> 5, col = 32 * b + (lane & 31);
+  const T* A = (const T*)a.R1;
+  T* Ap = (T*)a.R1p;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int hrow = (DT == 0) ? 16 * s + 8 * hf + e : 2 * s + hf;
+    T val = 0;
+    if (hrow < a.h && col < a.r) val = A[(size_t)hrow * a.r + col];
+    Ap[(size_t)gidx * EPL + e] = val;
+  }
+}
+
+}  // namespace more

@@ -1,0 +1,272 @@
+// more_route.hip -- host side of libmore_route.so: validation, workspace
+// layout and kernel dispatch for the C ABI in include/more_route.h.
+//
+// Every routing call enqueues two kernels on the caller's stream:
+//   1. pack_kernel: the expert sweep order (bias descending) and the weights
+//      in MFMA operand order, written into the caller's workspace;
+//   2. the fused router kernel (low rank or full rank).
+// Nothing is allocated, no state survives the call, no HIP call is made
+// before every argument has been checked.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "more_route.h"
+#include "more_device.h"
+#include "more_pack.h"
+#include "more_dispatch.h"
+
+using namespace more;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int kmax_for(int k) { return k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : 32; }
+int r16_for(int64_t r) { return r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8; }
+int waves_for(int kmax) { return waves_for_kmax(kmax); }
+size_t log_bytes(int kmax) { return (size_t)(2 * kmax + 8) * kWave * sizeof(float2); }
+
+struct Layout {
+  int NT, Mpad, r16, rb, ks1, ks2, epl, esize;
+  size_t off_r1p, off_r2p, off_bias, off_perm, total;
+};
+
+// Workspace layout of one call.  All offsets are 256-byte aligned.
+bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, Layout* L) {
+  L->NT = (int)((M + kTile - 1) / kTile);
+  L->Mpad = L->NT * kTile;
+  L->epl = (dt == MORE_DT_BF16) ? 8 : 1;
+  L->esize = (dt == MORE_DT_BF16) ? 2 : 4;
+  const size_t lane_bytes = (size_t)kWave * L->epl * L->esize;   // one K-step operand
+  if (fullrank) {
+    L->r16 = 0;
+    L->rb = 0;
+    L->ks1 = 0;
+    L->ks2 = (dt == MORE_DT_BF16) ? (int)((h + 15) / 16) : (int)((h + 1) / 2);
+  } else {
+    L->r16 = r16_for(r);
+    L->rb = (L->r16 + 1) / 2;
+    L->ks1 = (dt == MORE_DT_BF16) ? (int)((h + 15) / 16) : (int)((h + 1) / 2);
+    L->ks2 = (dt == MORE_DT_BF16) ? L->r16 : 8 * L->r16;
+  }
+  size_t off = 0;
+  L->off_r1p = off;
+  off += align_up((size_t)L->ks1 * L->rb * lane_bytes);
+  L->off_r2p = off;
+  off += align_up((size_t)L->NT * L->ks2 * lane_bytes);
+  L->off_bias = off;
+  off += align_up((size_t)L->NT * 2 * 16 * sizeof(float));
+  L->off_perm = off;
+  off += align_up((size_t)L->Mpad * sizeof(int));
+  L->total = off;
+  return true;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+more_status validate(int fullrank, more_dtype dt, const void* X, int64_t N, int64_t h,
+                     const void* A, int64_t r, const void* B, int64_t M, const float* bias,
+                     int32_t k, more_gate gate, const int32_t* idx, const float* gates,
+                     const float* logit, const float* lse) {
+  if (dt != MORE_DT_BF16 && dt != MORE_DT_F32) return MORE_ERR_BAD_DTYPE;
+  if (gate != MORE_GATE_TOPK_SOFTMAX && gate != MORE_GATE_FULL_SOFTMAX) return MORE_ERR_BAD_GATE;
+  if (N < 0 || h < 1 || M < 1 || (!fullrank && r < 1)) return MORE_ERR_BAD_SHAPE;
+  if (N > (1LL << 40) || h > (1 << 20) || M > (1 << 24) || (!fullrank && r > (1 << 20)))
+    return MORE_ERR_BAD_SHAPE;
+  if (k < 1 || k > MORE_MAX_K || (int64_t)k > M) return MORE_ERR_BAD_K;
+  if (h % 8 != 0) return MORE_ERR_UNSUPPORTED;
+  if (!fullrank && (r % 16 != 0 || r > MORE_MAX_R)) return MORE_ERR_UNSUPPORTED;
+  if (N == 0) return MORE_OK;
+  if (!X || !A || (!fullrank && !B) || !idx || !gates) return MORE_ERR_NULL_ARG;
+  if (!aligned16(X) || !aligned16(A) || (!fullrank && !aligned16(B)) || !aligned16(idx) ||
+      !aligned16(gates) || (bias && !aligned16(bias)) || (logit && !aligned16(logit)) ||
+      (lse && !aligned16(lse)))
+    return MORE_ERR_ALIGNMENT;
+  return MORE_OK;
+}
+
+// ---------------------------------------------------------------- dispatch
+lowrank_fn pick_lowrank(more_dtype dt, bool full, int kmax, int r16) {
+  if (dt == MORE_DT_BF16) return full ? pick_lowrank_bf16_full(kmax, r16) : pick_lowrank_bf16_topk(kmax, r16);
+  return pick_lowrank_f32(full, kmax, r16);
+}
+
+more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* B, const float* bias,
+                        int64_t h, int64_t r, int64_t M, const Layout& L, char* ws,
+                        hipStream_t stream) {
+  PackArgs p;
+  memset(&p, 0, sizeof p);
+  p.R1 = fullrank ? nullptr : A;
+  p.R2 = fullrank ? A : B;
+  p.bias = bias;
+  p.h = (int)h;
+  p.r = (int)r;
+  p.M = (int)M;
+  p.Mpad = L.Mpad;
+  p.NT = L.NT;
+  p.kdim = fullrank ? (int)h : (int)r;
+  p.ksteps2 = L.ks2;
+  p.ksteps1 = L.ks1;
+  p.rb = L.rb;
+  p.natural_k = fullrank;
+  p.rank_blocks = (L.Mpad + 63) / 64;
+  const int r1_total = L.ks1 * L.rb * kWave;
+  p.r1_blocks = fullrank ? 0 : (r1_total + 1023) / 1024;
+  p.R1p = ws + L.off_r1p;
+  p.R2p = ws + L.off_r2p;
+  p.biasp = (float*)(ws + L.off_bias);
+  p.perm = (int*)(ws + L.off_perm);
+  const int blocks = p.rank_blocks + p.r1_blocks;
+  if (dt == MORE_DT_BF16)
+    hipLaunchKernelGGL(pack_kernel<0>, dim3(blocks), dim3(1024), 0, stream, p);
+  else
+    hipLaunchKernelGGL(pack_kernel<1>, dim3(blocks), dim3(1024), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int more_abi_version(void) { return MORE_ABI_VERSION; }
+
+const char* more_status_str(more_status s) {
+  switch (s) {
+    case MORE_OK: return "ok";
+    case MORE_ERR_NULL_ARG: return "required pointer is NULL";
+    case MORE_ERR_BAD_SHAPE: return "bad shape (N < 0, h/M/r < 1 or too large)";
+    case MORE_ERR_BAD_K: return "bad k (need 1 <= k <= min(M, 32))";
+    case MORE_ERR_BAD_DTYPE: return "unknown dtype";
+    case MORE_ERR_BAD_GATE: return "unknown gate mode";
+    case MORE_ERR_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
+    case MORE_ERR_UNSUPPORTED: return "unsupported shape (need h % 8 == 0, r % 16 == 0, r <= 128)";
+    case MORE_ERR_HIP: return "HIP launch failed";
+    case MORE_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+size_t more_route_workspace_bytes(int fullrank, more_dtype dt, int64_t N, int64_t h, int64_t r,
+                                  int64_t M, int32_t k, more_gate gate, int has_bias) {
+  (void)N;
+  (void)has_bias;
+  if (dt != MORE_DT_BF16 && dt != MORE_DT_F32) return 0;
+  if (gate != MORE_GATE_TOPK_SOFTMAX && gate != MORE_GATE_FULL_SOFTMAX) return 0;
+  if (h < 1 || M < 1 || h % 8 != 0 || k < 1 || k > MORE_MAX_K || (int64_t)k > M) return 0;
+  if (!fullrank && (r < 16 || r % 16 != 0 || r > MORE_MAX_R)) return 0;
+  if (h > (1 << 20) || M > (1 << 24)) return 0;
+  Layout L;
+  make_layout(fullrank, dt, h, r, M, &L);
+  return L.total;
+}
+
+more_status more_lowrank_pack(more_dtype dt, const void* R1, int64_t h, int64_t r, const void* R2,
+                              int64_t M, const float* bias, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (dt != MORE_DT_BF16 && dt != MORE_DT_F32) return MORE_ERR_BAD_DTYPE;
+  if (h < 1 || M < 1 || r < 1 || h > (1 << 20) || M > (1 << 24) || r > (1 << 20)) return MORE_ERR_BAD_SHAPE;
+  if (h % 8 != 0 || r % 16 != 0 || r > MORE_MAX_R) return MORE_ERR_UNSUPPORTED;
+  if (!R1 || !R2) return MORE_ERR_NULL_ARG;
+  if (!aligned16(R1) || !aligned16(R2) || (bias && !aligned16(bias))) return MORE_ERR_ALIGNMENT;
+  Layout L;
+  make_layout(0, dt, h, r, M, &L);
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace % kAlign) != 0)
+    return MORE_ERR_WORKSPACE;
+  return launch_pack(dt, 0, R1, R2, bias, h, r, M, L, (char*)workspace, (hipStream_t)stream);
+}
+
+more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int64_t r,
+                                      int64_t M, int32_t k, more_gate gate, int32_t* topk_idx,
+                                      float* topk_gate, float* topk_logit, float* lse,
+                                      const void* workspace, size_t workspace_bytes, void* stream) {
+  // R1/R2 are not read here; a non-null placeholder keeps the shared validation.
+  more_status st = validate(0, dt, X, N, h, X, r, X, M, nullptr, k, gate, topk_idx, topk_gate,
+                            topk_logit, lse);
+  if (st != MORE_OK || N == 0) return st;
+  Layout L;
+  make_layout(0, dt, h, r, M, &L);
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace % kAlign) != 0)
+    return MORE_ERR_WORKSPACE;
+  const char* ws = (const char*)workspace;
+  const bool full = gate == MORE_GATE_FULL_SOFTMAX;
+  const int kmax = kmax_for(k);
+  const int waves = waves_for(kmax);
+  LowRankArgs a;
+  a.X = X;
+  a.N = N;
+  a.h = (int)h;
+  a.NT = L.NT;
+  a.k = k;
+  a.R1p = ws + L.off_r1p;
+  a.R2p = ws + L.off_r2p;
+  a.biasp = (const float*)(ws + L.off_bias);
+  a.perm = (const int*)(ws + L.off_perm);
+  a.out_idx = topk_idx;
+  a.out_gate = topk_gate;
+  a.out_logit = topk_logit;
+  a.out_lse = full ? lse : nullptr;
+  const int64_t per_block = (int64_t)waves * kTile;
+  const dim3 grid((unsigned)((N + per_block - 1) / per_block));
+  const size_t shmem = (size_t)waves * log_bytes(kmax);
+  hipLaunchKernelGGL(pick_lowrank(dt, full, kmax, L.r16), grid, dim3(64 * waves), shmem,
+                     (hipStream_t)stream, a);
+  return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+}
+
+more_status more_route_lowrank(more_dtype dt, const void* X, int64_t N, int64_t h, const void* R1,
+                               int64_t r, const void* R2, int64_t M, const float* bias, int32_t k,
+                               more_gate gate, int32_t* topk_idx, float* topk_gate,
+                               float* topk_logit, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  more_status st = validate(0, dt, X, N, h, R1, r, R2, M, bias, k, gate, topk_idx, topk_gate,
+                            topk_logit, lse);
+  if (st != MORE_OK || N == 0) return st;
+  st = more_lowrank_pack(dt, R1, h, r, R2, M, bias, workspace, workspace_bytes, stream);
+  if (st != MORE_OK) return st;
+  return more_lowrank_route_packed(dt, X, N, h, r, M, k, gate, topk_idx, topk_gate, topk_logit, lse,
+                                   workspace, workspace_bytes, stream);
+}
+
+more_status more_route_fullrank(more_dtype dt, const void* X, int64_t N, int64_t h, const void* W,
+                                int64_t M, const float* bias, int32_t k, more_gate gate,
+                                int32_t* topk_idx, float* topk_gate, float* topk_logit, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  more_status st = validate(1, dt, X, N, h, W, 0, nullptr, M, bias, k, gate, topk_idx, topk_gate,
+                            topk_logit, lse);
+  if (st != MORE_OK || N == 0) return st;
+  Layout L;
+  make_layout(1, dt, h, 0, M, &L);
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace % kAlign) != 0)
+    return MORE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  st = launch_pack(dt, 1, W, nullptr, bias, h, 0, M, L, ws, s);
+  if (st != MORE_OK) return st;
+  const bool full = gate == MORE_GATE_FULL_SOFTMAX;
+  const int kmax = kmax_for(k);
+  const int waves = waves_for(kmax);
+  FullRankArgs a;
+  a.X = X;
+  a.N = N;
+  a.h = (int)h;
+  a.NT = L.NT;
+  a.k = k;
+  a.KSW = L.ks2;
+  a.Wp = ws + L.off_r2p;
+  a.biasp = (const float*)(ws + L.off_bias);
+  a.perm = (const int*)(ws + L.off_perm);
+  a.out_idx = topk_idx;
+  a.out_gate = topk_gate;
+  a.out_logit = topk_logit;
+  a.out_lse = full ? lse : nullptr;
+  const int64_t per_block = (int64_t)waves * kTile;
+  const dim3 grid((unsigned)((N + per_block - 1) / per_block));
+  const size_t shmem = (size_t)waves * log_bytes(kmax);
+  hipLaunchKernelGGL(pick_fullrank((int)dt, full, kmax), grid, dim3(64 * waves), shmem, s, a);
+  return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+}
+
+}  // extern "C"

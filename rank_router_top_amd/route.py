@@ -1,0 +1,182 @@
+"""Thin ctypes binding of libmore_route.so (C ABI in include/more_route.h).
+
+Argument marshalling only: every step of routing runs in the HIP kernels of the
+library.  torch supplies device memory and the current stream.  There is no
+fallback: if the library is missing, or a call returns an error code, a
+RuntimeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmore_route.so")
+
+MORE_DT_BF16, MORE_DT_F32 = 0, 1
+MORE_GATE_TOPK_SOFTMAX, MORE_GATE_FULL_SOFTMAX = 0, 1
+MORE_OK = 0
+STATUS_NAMES = {0: "MORE_OK", 1: "MORE_ERR_NULL_ARG", 2: "MORE_ERR_BAD_SHAPE", 3: "MORE_ERR_BAD_K",
+                4: "MORE_ERR_BAD_DTYPE", 5: "MORE_ERR_BAD_GATE", 6: "MORE_ERR_WORKSPACE",
+                7: "MORE_ERR_UNSUPPORTED", 8: "MORE_ERR_HIP", 9: "MORE_ERR_ALIGNMENT"}
+EXPORTS = ("more_route_lowrank", "more_route_fullrank", "more_route_workspace_bytes",
+           "more_status_str", "more_abi_version", "more_lowrank_pack", "more_lowrank_route_packed")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MoreError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} -> {STATUS_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib() -> C.CDLL:
+    """Load libmore_route.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                                   "`python -m rank_router_top_amd.build` (no CPU fallback exists)")
+            L = C.CDLL(LIB_PATH)
+            p, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
+            L.more_route_lowrank.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, i32,
+                                             p, p, p, p, p, C.c_size_t, p]
+            L.more_route_lowrank.restype = C.c_int
+            L.more_route_fullrank.argtypes = [i32, p, i64, i64, p, i64, p, i32, i32,
+                                              p, p, p, p, p, C.c_size_t, p]
+            L.more_route_fullrank.restype = C.c_int
+            L.more_lowrank_pack.argtypes = [i32, p, i64, i64, p, i64, p, p, C.c_size_t, p]
+            L.more_lowrank_pack.restype = C.c_int
+            L.more_lowrank_route_packed.argtypes = [i32, p, i64, i64, i64, i64, i32, i32,
+                                                    p, p, p, p, p, C.c_size_t, p]
+            L.more_lowrank_route_packed.restype = C.c_int
+            L.more_route_workspace_bytes.argtypes = [C.c_int, i32, i64, i64, i64, i64, i32, i32, C.c_int]
+            L.more_route_workspace_bytes.restype = C.c_size_t
+            L.more_status_str.argtypes = [C.c_int]
+            L.more_status_str.restype = C.c_char_p
+            L.more_abi_version.restype = C.c_int
+            _lib = L
+    return _lib
+
+
+def status_str(code: int) -> str:
+    return lib().more_status_str(code).decode()
+
+
+def _check(fn: str, code: int):
+    if code != MORE_OK:
+        raise MoreError(fn, code, status_str(code))
+
+
+def workspace_bytes(fullrank: bool, dt: int, N: int, h: int, r: int, M: int, k: int, gate: int,
+                    has_bias: bool) -> int:
+    return int(lib().more_route_workspace_bytes(int(fullrank), dt, N, h, r, M, k, gate, int(has_bias)))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MORE_DT_BF16
+    if t.dtype == torch.float32:
+        return MORE_DT_F32
+    raise TypeError(f"unsupported tensor dtype {t.dtype}: bfloat16 or float32 expected")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _outputs(X, k, want_logit, want_lse, out):
+    import torch
+    N = X.shape[0]
+    if out is not None:
+        return out
+    dev = X.device
+    return dict(idx=torch.empty((N, k), dtype=torch.int32, device=dev),
+                gate=torch.empty((N, k), dtype=torch.float32, device=dev),
+                logit=torch.empty((N, k), dtype=torch.float32, device=dev) if want_logit else None,
+                lse=torch.empty((N,), dtype=torch.float32, device=dev) if want_lse else None)
+
+
+def _workspace(nbytes, workspace, device):
+    import torch
+    if workspace is not None:
+        return workspace
+    return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
+
+
+def route_lowrank(X, R1, R2, bias, k: int, gate: int = MORE_GATE_TOPK_SOFTMAX, *, out=None,
+                  workspace=None, want_logit: bool = True, want_lse: bool = True, stream=None) -> dict:
+    """more_route_lowrank on torch device tensors.  Returns dict(idx, gate, logit, lse)."""
+    dt = _dtype_code(X)
+    N, h = X.shape
+    r, M = R2.shape
+    want_lse = want_lse and gate == MORE_GATE_FULL_SOFTMAX
+    o = _outputs(X, k, want_logit, want_lse, out)
+    nb = workspace_bytes(False, dt, N, h, r, M, k, gate, bias is not None)
+    ws = _workspace(nb, workspace, X.device)
+    _check("more_route_lowrank", lib().more_route_lowrank(
+        dt, _ptr(X), N, h, _ptr(R1), r, _ptr(R2), M, _ptr(bias), k, gate,
+        _ptr(o["idx"]), _ptr(o["gate"]), _ptr(o.get("logit")), _ptr(o.get("lse")),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return o
+
+
+def pack_lowrank(R1, R2, bias, workspace, stream=None):
+    """more_lowrank_pack: pack static low-rank weights into `workspace` (uint8 device tensor)."""
+    dt = _dtype_code(R1)
+    h, r = R1.shape
+    M = R2.shape[1]
+    _check("more_lowrank_pack", lib().more_lowrank_pack(
+        dt, _ptr(R1), h, r, _ptr(R2), M, _ptr(bias), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def route_lowrank_packed(X, r: int, M: int, k: int, gate: int, workspace, *, out=None,
+                         want_logit: bool = True, want_lse: bool = True, stream=None) -> dict:
+    """more_lowrank_route_packed: route X against weights packed by pack_lowrank."""
+    dt = _dtype_code(X)
+    N, h = X.shape
+    want_lse = want_lse and gate == MORE_GATE_FULL_SOFTMAX
+    o = _outputs(X, k, want_logit, want_lse, out)
+    _check("more_lowrank_route_packed", lib().more_lowrank_route_packed(
+        dt, _ptr(X), N, h, r, M, k, gate, _ptr(o["idx"]), _ptr(o["gate"]), _ptr(o.get("logit")),
+        _ptr(o.get("lse")), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return o
+
+
+def route_fullrank(X, W, bias, k: int, gate: int = MORE_GATE_TOPK_SOFTMAX, *, out=None,
+                   workspace=None, want_logit: bool = True, want_lse: bool = True, stream=None) -> dict:
+    """more_route_fullrank on torch device tensors.  Returns dict(idx, gate, logit, lse)."""
+    dt = _dtype_code(X)
+    N, h = X.shape
+    M = W.shape[1]
+    want_lse = want_lse and gate == MORE_GATE_FULL_SOFTMAX
+    o = _outputs(X, k, want_logit, want_lse, out)
+    nb = workspace_bytes(True, dt, N, h, 0, M, k, gate, bias is not None)
+    ws = _workspace(nb, workspace, X.device)
+    _check("more_route_fullrank", lib().more_route_fullrank(
+        dt, _ptr(X), N, h, _ptr(W), M, _ptr(bias), k, gate,
+        _ptr(o["idx"]), _ptr(o["gate"]), _ptr(o.get("logit")), _ptr(o.get("lse")),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return o
+
+
+def to_device(a, device):
+    """numpy input (bf16 bits as uint16, or fp32) -> torch tensor on `device`."""
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)

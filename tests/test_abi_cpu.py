@@ -1,0 +1,86 @@
+"""The C-ABI library: loads without a GPU, exports what include/more_route.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from rank_router_top_amd import route as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "more_route.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(R.LIB_PATH),
+                                reason="libmore_route.so not built (python -m rank_router_top_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(more_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(R.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.CDLL(R.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert R.lib().more_abi_version() == 1
+    for code in range(10):
+        s = R.status_str(code)
+        assert s and s != "unknown status"
+    assert R.status_str(99) == "unknown status"
+
+
+def test_workspace_size_is_pure_host_and_rejects_bad_args():
+    ws = R.workspace_bytes(False, R.MORE_DT_BF16, 262144, 2048, 32, 4096, 8, 0, True)
+    # packed R1 (128 KiB) + packed R2 (256 KiB) + bias tiles + sweep order
+    assert 128 * 1024 + 256 * 1024 <= ws < 128 * 1024 + 256 * 1024 + 64 * 1024
+    assert ws % 256 == 0
+    assert R.workspace_bytes(True, R.MORE_DT_BF16, 100, 2048, 0, 4096, 8, 0, True) >= 2048 * 4096 * 2
+    assert R.workspace_bytes(False, R.MORE_DT_BF16, 1, 2048, 24, 4096, 8, 0, False) == 0   # r % 16
+    assert R.workspace_bytes(False, R.MORE_DT_BF16, 1, 2044, 32, 4096, 8, 0, False) == 0   # h % 8
+    assert R.workspace_bytes(False, R.MORE_DT_BF16, 1, 2048, 32, 4096, 33, 0, False) == 0  # k
+    assert R.workspace_bytes(False, 7, 1, 2048, 32, 4096, 8, 0, False) == 0                # dtype
+
+
+FAKE = C.c_void_p(0x1000)     # aligned non-null host address: never dereferenced on error paths
+ODD = C.c_void_p(0x1004)
+
+
+def call_lowrank(dt=0, X=FAKE, N=64, h=64, R1=FAKE, r=16, R2=FAKE, M=32, bias=None, k=4, gate=0,
+                 idx=FAKE, g=FAKE, logit=None, lse=None, ws=FAKE, ws_bytes=1 << 20):
+    return R.lib().more_route_lowrank(dt, X, N, h, R1, r, R2, M, bias, k, gate, idx, g, logit, lse,
+                                      ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), 4), (dict(gate=3), 5), (dict(N=-1), 2), (dict(h=0), 2), (dict(M=0), 2),
+    (dict(r=0), 2), (dict(k=0), 3), (dict(k=33), 3), (dict(k=40, M=39), 3), (dict(k=5, M=4), 3),
+    (dict(h=60), 7), (dict(r=24), 7), (dict(r=144), 7), (dict(X=None), 1), (dict(R1=None), 1),
+    (dict(R2=None), 1), (dict(idx=None), 1), (dict(g=None), 1), (dict(X=ODD), 9),
+    (dict(idx=ODD), 9), (dict(ws=None), 6), (dict(ws_bytes=100), 6),
+    (dict(ws=C.c_void_p(0x1010)), 6),
+])
+def test_lowrank_rejects_bad_arguments_before_any_hip_call(kw, code):
+    assert call_lowrank(**kw) == code
+
+
+def test_empty_batch_is_a_noop():
+    assert call_lowrank(N=0, X=None, idx=None, g=None) == 0
+
+
+def test_fullrank_rejects_bad_arguments():
+    L = R.lib()
+    f = L.more_route_fullrank
+    assert f(0, FAKE, 64, 64, FAKE, 32, None, 33, 0, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == 3
+    assert f(0, FAKE, 64, 63, FAKE, 32, None, 4, 0, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == 7
+    assert f(0, None, 64, 64, FAKE, 32, None, 4, 0, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == 1
+    assert f(0, FAKE, 64, 64, FAKE, 32, None, 4, 0, FAKE, FAKE, None, None, FAKE, 16, None) == 6

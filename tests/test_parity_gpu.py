@@ -1,0 +1,246 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case prints its name before running so that a failing GPU step can be
+identified from the log.  Sizes are reduced from the full workloads so the
+oracle finishes in seconds, while still spanning many expert tiles, several
+workgroups and a ragged token tail.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from rank_router_top_amd import configs as CF
+from rank_router_top_amd import inputs as I
+from rank_router_top_amd import route as R
+
+from parity import compare, gap_clear
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_np(o):
+    return {k: (None if v is None else v.cpu().numpy()) for k, v in o.items()}
+
+
+def run_lowrank(X, R1, R2, b, k, gate):
+    d = [R.to_device(a, DEV) for a in (X, R1, R2, b)]
+    out = R.route_lowrank(*d, k, gate)
+    torch.cuda.synchronize()
+    return to_np(out)
+
+
+def run_fullrank(X, W, b, k, gate):
+    d = [R.to_device(a, DEV) for a in (X, W, b)]
+    out = R.route_fullrank(*d, k, gate)
+    torch.cuda.synchronize()
+    return to_np(out)
+
+
+def check_lowrank(oracle_lib, X, R1, R2, b, k, gate, label, logit_tol=2e-4):
+    say(f"{label}: N={X.shape[0]} h={X.shape[1]} r={R1.shape[1]} M={R2.shape[1]} k={k} gate={gate}")
+    g = run_lowrank(X, R1, R2, b, k, gate)
+    o = oracle_lib.route_lowrank(X, R1, R2, b, k, gate)
+    res = compare(o, g, k, gate == R.MORE_GATE_FULL_SOFTMAX, logit_tol, label)
+    say(f"{label}: ok {res}")
+    return o, g
+
+
+# --------------------------------------------------------------------------- configs
+CASES = [
+    (CF.TINY, 256, CF.GATE_TOPK_SOFTMAX),
+    (CF.PREFILL_H512, 4096 + 37, CF.GATE_TOPK_SOFTMAX),
+    (CF.PREFILL_H512, 2048 + 99, CF.GATE_FULL_SOFTMAX),
+    (CF.HEADLINE, 2048 + 5, CF.GATE_TOPK_SOFTMAX),
+    (CF.HEADLINE, 1024 + 77, CF.GATE_FULL_SOFTMAX),
+    (CF.RANK16, 1024 + 1, CF.GATE_TOPK_SOFTMAX),
+    (CF.RANK64, 1024 + 31, CF.GATE_TOPK_SOFTMAX),
+    (CF.RANK128, 1024 + 64, CF.GATE_TOPK_SOFTMAX),
+    (CF.MANY_DECODE, 256, CF.GATE_FULL_SOFTMAX),
+]
+
+
+@pytest.mark.parametrize("cfg,n,gate", CASES, ids=[f"{c.name}-{n}-g{g}" for c, n, g in CASES])
+def test_lowrank_configs(oracle_lib, cfg, n, gate):
+    X = cfg.x_rows(0, 0, n, n_total=cfg.N)
+    R1, R2, b = cfg.weights(0)
+    check_lowrank(oracle_lib, X, R1, R2, b, cfg.k, gate, cfg.name)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_headline_other_seeds(oracle_lib, seed):
+    cfg = CF.HEADLINE
+    X = cfg.x_rows(seed, 0, 1024, n_total=cfg.N)
+    R1, R2, b = cfg.weights(seed)
+    check_lowrank(oracle_lib, X, R1, R2, b, cfg.k, CF.GATE_TOPK_SOFTMAX, f"headline-seed{seed}")
+
+
+@pytest.mark.parametrize("gate", [CF.GATE_TOPK_SOFTMAX, CF.GATE_FULL_SOFTMAX])
+def test_fullrank_baseline(oracle_lib, gate):
+    cfg = CF.FULLRANK
+    n = 512 + 3
+    X = cfg.x_rows(0, 0, n, n_total=cfg.N)
+    W, _, b = cfg.weights(0)
+    say(f"fullrank: N={n} gate={gate}")
+    g = run_fullrank(X, W, b, cfg.k, gate)
+    o = oracle_lib.route_fullrank(X, W, b, cfg.k, gate)
+    say(f"fullrank: ok {compare(o, g, cfg.k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, 'fullrank')}")
+
+
+def test_fullrank_tiny_fp32(oracle_lib):
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((200, 64)).astype(np.float32)
+    W = (rng.standard_normal((64, 77)) / 8).astype(np.float32)
+    b = rng.standard_normal(77).astype(np.float32)
+    say("fullrank fp32 tiny")
+    g = run_fullrank(X, W, b, 5, 0)
+    o = oracle_lib.route_fullrank(X, W, b, 5, 0)
+    compare(o, g, 5, False, 1e-5, "fullrank-f32")
+
+
+# ------------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("N,h,r,M,k,dt", [
+    (1, 64, 16, 40, 3, "bf16"),        # single token
+    (33, 8, 16, 32, 32, "bf16"),       # k = M = 32, h = 8 (half a K-step)
+    (40, 8, 16, 33, 30, "bf16"),       # M one past a tile, k close to M
+    (70, 136, 32, 100, 1, "bf16"),     # k = 1, h % 16 = 8, ragged M
+    (130, 256, 48, 1000, 32, "bf16"),  # k = 32 (largest list), r = 48 padded to 64
+    (97, 96, 16, 257, 16, "f32"),      # fp32 path, k = 16
+    (64, 64, 128, 64, 32, "f32"),      # fp32, r = 128, k = M/2
+])
+def test_edge_shapes(oracle_lib, N, h, r, M, k, dt):
+    rng = np.random.default_rng(N * 7 + M)
+    X = rng.standard_normal((N, h))
+    X /= np.sqrt(np.mean(X * X, axis=1, keepdims=True))
+    R1 = rng.standard_normal((h, r)) / math.sqrt(h)
+    R2 = rng.standard_normal((r, M)) / math.sqrt(r)
+    b = (rng.standard_normal(M) * 0.7).astype(np.float32)
+    conv = (lambda a: I.f32_to_bf16_bits(a.astype(np.float32))) if dt == "bf16" else (lambda a: a.astype(np.float32))
+    X, R1, R2 = conv(X), conv(R1), conv(R2)
+    for gate in (0, 1):
+        check_lowrank(oracle_lib, X, R1, R2, b, k, gate, f"edge-{N}x{h}x{r}x{M}-k{k}-{dt}",
+                      logit_tol=2e-4 if dt == "bf16" else 1e-5)
+
+
+def test_exact_ties_lower_index_wins(oracle_lib):
+    """Duplicated R2 columns (and equal biases) give bitwise-equal logits; the
+    lower expert index must win, with and without the bias-ordered sweep."""
+    rng = np.random.default_rng(9)
+    h, r, M = 64, 16, 256
+    X = I.f32_to_bf16_bits(rng.standard_normal((300, h)).astype(np.float32))
+    R1 = I.f32_to_bf16_bits((rng.standard_normal((h, r)) / 8).astype(np.float32))
+    base = rng.standard_normal((r, 16)).astype(np.float32)
+    cols = rng.integers(0, 16, M)
+    R2 = I.f32_to_bf16_bits(base[:, cols])
+    bias_base = rng.standard_normal(16).astype(np.float32)
+    for b in (None, bias_base[cols]):
+        for k in (1, 5, 8, 20):
+            say(f"ties k={k} bias={b is not None}")
+            g = run_lowrank(X, R1, R2, b, k, 0)
+            o = oracle_lib.route_lowrank(X, R1, R2, b, k, 0)
+            # logits of equal columns are bitwise equal on both sides, so the full
+            # ordered index lists must agree wherever the oracle's distinct values
+            # are separated by more than the GPU's rounding
+            assert np.array_equal(g["idx"], o["idx"]), "tie rule violated"
+
+
+def test_all_equal_logits(oracle_lib):
+    """Zero tokens and no bias: every logit is 0.  The top-k must be experts
+    0..k-1 with uniform gates (stresses the log's tie pruning)."""
+    N, h, r, M = 64, 32, 16, 4096
+    X = np.zeros((N, h), np.uint16)
+    rng = np.random.default_rng(0)
+    R1 = I.f32_to_bf16_bits(rng.standard_normal((h, r)).astype(np.float32))
+    R2 = I.f32_to_bf16_bits(rng.standard_normal((r, M)).astype(np.float32))
+    for k in (1, 8, 32):
+        say(f"all-equal k={k}")
+        g = run_lowrank(X, R1, R2, None, k, 0)
+        assert np.array_equal(g["idx"], np.tile(np.arange(k, dtype=np.int32), (N, 1)))
+        assert np.allclose(g["gate"], 1.0 / k, atol=1e-6)
+        gf = run_lowrank(X, R1, R2, None, k, 1)
+        assert np.allclose(gf["gate"], 1.0 / M, rtol=1e-5)
+        assert np.allclose(gf["lse"], math.log(M), atol=1e-5)
+
+
+def test_planted_set_fp32(oracle_lib):
+    """Thm. 4 construction (App. J) at r = M: top-k = S exactly, equal logits
+    inside S listed by ascending index, gates 1/k."""
+    M, k, N = 64, 6, 40
+    rho = math.sqrt(1 / k + 1 / (M - k))
+    rng = np.random.default_rng(1)
+    X = np.full((N, M), -1.0 / ((M - k) * rho), np.float32)
+    sets = []
+    for n in range(N):
+        S = np.sort(rng.choice(M, k, replace=False))
+        X[n, S] = np.float32(1.0 / (k * rho))
+        sets.append(S)
+    eye = np.eye(M, dtype=np.float32)
+    say("planted set")
+    g = run_lowrank(X, eye, eye, None, k, 0)
+    assert np.array_equal(g["idx"], np.array(sets, np.int32))
+    assert np.allclose(g["gate"], 1.0 / k, atol=1e-6)
+
+
+def test_hypercube_router(oracle_lib):
+    """Prop. 1 construction: sign-vector experts (exact in bf16); top-1 is the
+    sign pattern of z."""
+    r, h, N = 8, 64, 512
+    M = 2 ** r
+    R1 = np.zeros((h, 16), np.float32)
+    R1[:r, :r] = np.eye(r)
+    bits = (np.arange(M)[None, :] >> np.arange(r)[:, None]) & 1
+    R2 = np.zeros((16, M), np.float32)
+    R2[:r] = np.where(bits == 1, 1.0, -1.0)
+    X = I.make_x(3, 30, N, h, I.DT_BF16, False)
+    z = I.to_f64(X, I.DT_BF16)[:, :r]
+    say("hypercube")
+    g = run_lowrank(X, I.f32_to_bf16_bits(R1), I.f32_to_bf16_bits(R2), None, 4, 0)
+    top1 = ((z > 0).astype(np.int64) << np.arange(r)).sum(1)
+    assert np.array_equal(g["idx"][:, 0], top1.astype(np.int32))
+    o = oracle_lib.route_lowrank(X, I.f32_to_bf16_bits(R1), I.f32_to_bf16_bits(R2), None, 4, 0)
+    compare(o, g, 4, False, 2e-4, "hypercube")
+
+
+def test_expert_permutation_equivariance():
+    """Lemma 3: permuting R2's columns and the bias permutes the indices; gates unchanged."""
+    cfg = CF.HEADLINE
+    X = cfg.x_rows(0, 0, 1024, n_total=cfg.N)
+    R1, R2, b = cfg.weights(0)
+    perm = np.random.default_rng(5).permutation(cfg.M)
+    say("equivariance")
+    a = run_lowrank(X, R1, R2, b, cfg.k, 0)
+    c = run_lowrank(X, R1, np.ascontiguousarray(R2[:, perm]), b[perm], cfg.k, 0)
+    assert np.array_equal(np.sort(perm[c["idx"]], 1), np.sort(a["idx"], 1))
+    assert np.allclose(a["gate"], c["gate"], atol=1e-6)
+
+
+def test_deterministic_bitwise():
+    """No atomics on the path: two runs are bit-identical."""
+    cfg = CF.HEADLINE
+    X = cfg.x_rows(0, 0, 4096 + 3, n_total=cfg.N)
+    R1, R2, b = cfg.weights(0)
+    say("determinism")
+    a = run_lowrank(X, R1, R2, b, cfg.k, 0)
+    c = run_lowrank(X, R1, R2, b, cfg.k, 0)
+    for key in ("idx", "gate", "logit"):
+        assert np.array_equal(a[key], c[key])
+
+
+def test_gap_rule_excludes_few_tokens(oracle_lib):
+    """Sanity of the comparison itself on the headline shape: the gap rule
+    excludes a minority of tokens, so parity is tested on most of them."""
+    cfg = CF.HEADLINE
+    X = cfg.x_rows(0, 0, 2048, n_total=cfg.N)
+    R1, R2, b = cfg.weights(0)
+    o = oracle_lib.route_lowrank(X, R1, R2, b, cfg.k, 0)
+    assert gap_clear(o).mean() > 0.8
