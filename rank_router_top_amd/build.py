@@ -28,6 +28,11 @@ ARCH = "gfx950"
 
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # no NaN ever reaches the kernels (finite inputs; -inf is used, NaN is not):
+          # lets v_max/v_med3 run without canonicalising their operands
+          "-fno-honor-nans",
+          # keep MFMA accumulators in VGPRs: the top-k reads every logit with VALU ops
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-function"]
 
 

@@ -59,6 +59,53 @@ struct LogRef {
   float2* base;   // this wave's log: entry c of lane l at base[c * 64 + l]
 };
 
+// Drop log entries that can no longer reach the top-k (value < thr); returns
+// the new entry count.  When exact ties at thr keep the log nearly full, keep
+// only the k ties of lowest expert index (the tie rule): entries of higher rank
+// among the ties can never be selected.  Called with the whole wave active.
+// Kept out of line: it is rare, and its perm[] lookups (global loads) would
+// otherwise force conservative memory waits into the sweep loops.
+__device__ __noinline__ int compact_log(float2* base, int lane, int cnt, float thr,
+                                        const int* __restrict__ perm, int k, int cap) {
+  int w = 0;
+  for (int c = 0; c < cnt; ++c) {
+    const float2 e = base[c * kWave + lane];
+    if (e.x >= thr) {
+      base[w * kWave + lane] = e;
+      ++w;
+    }
+  }
+  cnt = w;
+  if (any_lane(cnt > cap - 8)) {
+    if (cnt > cap - 8) {
+      // pass 1: knock out ties of rank >= k (rank by original expert index)
+      for (int c = 0; c < cnt; ++c) {
+        const float2 e = base[c * kWave + lane];
+        if (e.x == thr) {
+          const int oi = perm[__float_as_int(e.y)];
+          int rank = 0;
+          for (int c2 = 0; c2 < cnt; ++c2) {
+            const float2 e2 = base[c2 * kWave + lane];
+            if (e2.x == thr && perm[__float_as_int(e2.y)] < oi) ++rank;
+          }
+          if (rank >= k) base[c * kWave + lane] = make_float2(-__builtin_inff(), e.y);
+        }
+      }
+      // pass 2: squeeze out the knocked-out entries
+      w = 0;
+      for (int c = 0; c < cnt; ++c) {
+        const float2 e = base[c * kWave + lane];
+        if (e.x >= thr) {
+          base[w * kWave + lane] = e;
+          ++w;
+        }
+      }
+      cnt = w;
+    }
+  }
+  return cnt;
+}
+
 template <int KMAX, int CAP>
 struct SweepState {
   float L[KMAX];   // descending; the first KMAX-k slots hold +inf (runtime k < KMAX)
@@ -87,49 +134,8 @@ struct SweepState {
     thr = fmaxf(L[KMAX - 1], thr_p);
   }
 
-  // Drop log entries that can no longer reach the top-k (value < thr).  When
-  // exact ties at thr keep the log full, keep only the k ties of lowest expert
-  // index (the tie rule); entries of higher rank among the ties can never be
-  // selected.  Called with the whole wave active.
-  __device__ void compact(LogRef lg, int lane, const int* __restrict__ perm, int k) {
-    int w = 0;
-    for (int c = 0; c < CAP; ++c) {
-      if (c < cnt) {
-        float2 e = lg.base[c * kWave + lane];
-        if (e.x >= thr) {
-          lg.base[w * kWave + lane] = e;
-          ++w;
-        }
-      }
-    }
-    cnt = w;
-    if (any_lane(cnt > CAP - 8)) {
-      if (cnt > CAP - 8) {
-        // pass 1: knock out ties of rank >= k (rank by original expert index)
-        for (int c = 0; c < cnt; ++c) {
-          float2 e = lg.base[c * kWave + lane];
-          if (e.x == thr) {
-            const int oi = perm[__float_as_int(e.y)];
-            int rank = 0;
-            for (int c2 = 0; c2 < cnt; ++c2) {
-              float2 e2 = lg.base[c2 * kWave + lane];
-              if (e2.x == thr && perm[__float_as_int(e2.y)] < oi) ++rank;
-            }
-            if (rank >= k) lg.base[c * kWave + lane] = make_float2(-__builtin_inff(), e.y);
-          }
-        }
-        // pass 2: squeeze out the knocked-out entries
-        w = 0;
-        for (int c = 0; c < cnt; ++c) {
-          float2 e = lg.base[c * kWave + lane];
-          if (e.x >= thr) {
-            lg.base[w * kWave + lane] = e;
-            ++w;
-          }
-        }
-        cnt = w;
-      }
-    }
+  __device__ __forceinline__ void compact(LogRef lg, int lane, const int* __restrict__ perm, int k) {
+    cnt = compact_log(lg.base, lane, cnt, thr, perm, k, CAP);
   }
 
   // One 32-expert tile: acc holds this lane's 16 logits (bias included,
@@ -188,6 +194,71 @@ __device__ __forceinline__ void ordered_insert(float (&V)[KMAX], int (&IX)[KMAX]
     V[0] = x;
     IX[0] = ix;
   }
+}
+
+// End of a token block: merge the two half-token logs of every token, order
+// by (logit desc, expert index asc), form the gates and store.  Must be called
+// with the whole wave active (the final compaction uses wave-wide votes).
+template <int KMAX, int CAP, bool FULL>
+__device__ __forceinline__ void finish_tokens(SweepState<KMAX, CAP>& st, LogRef lg, int lane,
+                                              bool hi_half, bool rowok, long long n,
+                                              const int* __restrict__ perm, int k, int* out_idx,
+                                              float* out_gate, float* out_logit, float* out_lse) {
+  st.thr_p = partner_f32(st.L[KMAX - 1], hi_half);
+  st.thr = fmaxf(st.L[KMAX - 1], st.thr_p);
+  st.compact(lg, lane, perm, k);
+  const int cnt_p = (int)partner_u32((uint32_t)st.cnt, hi_half);
+  float lse = 0.f;
+  if (FULL) {
+    // eq. (8) across the two halves: one running max and one normaliser per token
+    const float mp = partner_f32(st.m, hi_half), Zp = partner_f32(st.Z, hi_half);
+    const float mm = fmaxf(st.m, mp);
+    const float Zt = st.Z * __builtin_amdgcn_exp2f((st.m - mm) * kLog2e) +
+                     Zp * __builtin_amdgcn_exp2f((mp - mm) * kLog2e);
+    lse = mm + __builtin_amdgcn_logf(Zt) * kLn2;
+  }
+  if (hi_half || !rowok) return;
+  float V[KMAX];
+  int IX[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    V[j] = -__builtin_inff();
+    IX[j] = 0x7fffffff;
+  }
+  for (int c = 0; c < st.cnt; ++c) {
+    const float2 e = lg.base[c * kWave + lane];
+    ordered_insert<KMAX>(V, IX, e.x, perm[__float_as_int(e.y)]);
+  }
+  for (int c = 0; c < cnt_p; ++c) {
+    const float2 e = lg.base[c * kWave + lane + 32];
+    ordered_insert<KMAX>(V, IX, e.x, perm[__float_as_int(e.y)]);
+  }
+  float w[KMAX];
+  if (FULL) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) w[j] = __builtin_amdgcn_exp2f((V[j] - lse) * kLog2e);
+  } else {
+    // Fig. 12: softmax over the k selected logits, max subtracted
+    float denom = 0.f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      w[j] = (j < k) ? __builtin_amdgcn_exp2f((V[j] - V[0]) * kLog2e) : 0.f;
+      denom += w[j];
+    }
+    const float inv = 1.f / denom;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) w[j] *= inv;
+  }
+  const size_t o = (size_t)n * k;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      out_idx[o + j] = IX[j];
+      out_gate[o + j] = w[j];
+      if (out_logit) out_logit[o + j] = V[j];
+    }
+  }
+  if (FULL && out_lse) out_lse[n] = lse;
 }
 
 }  // namespace more

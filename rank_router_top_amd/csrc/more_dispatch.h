@@ -3,6 +3,7 @@
 #pragma once
 #include "more_lowrank.h"
 #include "more_fullrank.h"
+#include "more_stream.h"
 
 namespace more {
 
@@ -12,6 +13,14 @@ typedef void (*fullrank_fn)(FullRankArgs);
 // Waves per workgroup: each wave's log takes (2*KMAX+8)*512 bytes of LDS;
 // keep a workgroup within 64 KiB.
 constexpr int waves_for_kmax(int kmax) { return kmax <= 8 ? 4 : (kmax == 16 ? 2 : 1); }
+
+typedef void (*stream_fn)(StreamArgs);
+
+// Ring depth of the streaming kernel: 8 K-steps ahead for r <= 32, 4 for r = 64.
+constexpr int stream_depth(int r16) { return r16 <= 2 ? 8 : 4; }
+// The streaming kernel covers bf16 storage with r <= 64.
+constexpr bool stream_supported(int r16) { return r16 <= 4; }
+stream_fn pick_stream(bool full, int kmax, int r16);
 
 lowrank_fn pick_lowrank_bf16_topk(int kmax, int r16);
 lowrank_fn pick_lowrank_bf16_full(int kmax, int r16);

@@ -74,59 +74,8 @@ __global__ __launch_bounds__(64 * WAVES) void fullrank_kernel(FullRankArgs a) {
     }
   }
 
-  st.thr_p = partner_f32(st.L[KMAX - 1], hi);
-  st.thr = fmaxf(st.L[KMAX - 1], st.thr_p);
-  st.compact(lg, lane, a.perm, a.k);
-  const int cnt_p = (int)partner_u32((uint32_t)st.cnt, hi);
-  float lse = 0.f;
-  if (FULL) {
-    const float mp = partner_f32(st.m, hi), Zp = partner_f32(st.Z, hi);
-    const float mm = fmaxf(st.m, mp);
-    const float Zt = st.Z * __builtin_amdgcn_exp2f((st.m - mm) * kLog2e) +
-                     Zp * __builtin_amdgcn_exp2f((mp - mm) * kLog2e);
-    lse = mm + __builtin_amdgcn_logf(Zt) * kLn2;
-  }
-  if (hi || !rowok) return;
-  float V[KMAX];
-  int IX[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    V[j] = -__builtin_inff();
-    IX[j] = 0x7fffffff;
-  }
-  for (int c = 0; c < st.cnt; ++c) {
-    const float2 e = lg.base[c * kWave + lane];
-    ordered_insert<KMAX>(V, IX, e.x, a.perm[__float_as_int(e.y)]);
-  }
-  for (int c = 0; c < cnt_p; ++c) {
-    const float2 e = lg.base[c * kWave + lane + 32];
-    ordered_insert<KMAX>(V, IX, e.x, a.perm[__float_as_int(e.y)]);
-  }
-  float w[KMAX];
-  if (FULL) {
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) w[j] = __builtin_amdgcn_exp2f((V[j] - lse) * kLog2e);
-  } else {
-    float denom = 0.f;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      w[j] = (j < a.k) ? __builtin_amdgcn_exp2f((V[j] - V[0]) * kLog2e) : 0.f;
-      denom += w[j];
-    }
-    const float inv = 1.f / denom;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) w[j] *= inv;
-  }
-  const size_t o = (size_t)n * a.k;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < a.k) {
-      a.out_idx[o + j] = IX[j];
-      a.out_gate[o + j] = w[j];
-      if (a.out_logit) a.out_logit[o + j] = V[j];
-    }
-  }
-  if (FULL && a.out_lse) a.out_lse[n] = lse;
+  finish_tokens<KMAX, CAP, FULL>(st, lg, lane, hi, rowok, n, a.perm, a.k, a.out_idx, a.out_gate,
+                                 a.out_logit, a.out_lse);
 }
 
 }  // namespace more

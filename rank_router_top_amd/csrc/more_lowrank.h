@@ -11,15 +11,20 @@
 // barrier.  Per wave:
 //   phase 1  z^T (r x 32) = R1^T X^T with v_mfma_f32_32x32x16_bf16: each lane
 //            streams 16 bytes of one X row per K-step (16 hidden units), with
-//            a double-buffered group of K-steps in flight, and reads the
-//            packed R1 operand (L2-resident).  z stays in the accumulators.
+//            a double-buffered group of K-steps in flight (unconditional loads
+//            from clamped addresses, so the group really stays in flight), and
+//            reads the packed R1 operand (L2-resident).  z stays in registers.
 //   split    z -> bf16 hi + bf16 lo (both round to nearest even).  The paper
 //            narrows z to bf16 once; keeping the residual makes the logits
 //            accurate to ~2^-17 relative, so the selected set is exact except
 //            on near-ties far below the logit spread.
-//   phase 2  per tile of 32 experts: acc = bias (C operand, -inf on padding);
-//            acc += R2^T z_hi; acc += R2^T z_lo  -> 32 experts x 32 tokens of
-//            logits in registers; then the streaming top-k of more_device.h.
+//   phase 2  per tile of 32 experts: acc = A_bias x ones (the bias as a bf16
+//            hi + lo pair in two K-slots: one extra MFMA per tile instead of
+//            64 bytes of bias per lane; -inf on padding rows); acc += R2^T z_hi;
+//            acc += R2^T z_lo -> 32 experts x 32 tokens of logits in registers;
+//            then the streaming top-k of more_device.h.  The MFMAs of tile t+1
+//            are issued before the top-k work on tile t, and the weight
+//            operands are fetched two tiles ahead.
 //   end      merge the two half-token logs, order by (logit desc, expert
 //            index asc), form the gates, store.
 #pragma once
@@ -36,7 +41,8 @@ struct LowRankArgs {
   int k;
   const void* R1p;
   const void* R2p;
-  const float* biasp;
+  const float* biasp;      // fp32 kernels: bias in accumulator layout
+  const uint32_t* biasq;   // bf16 kernels: bias as a bf16 hi/lo MFMA operand
   const int* perm;
   int* out_idx;
   float* out_gate;
@@ -68,28 +74,28 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_kernel(LowRankArgs a) {
     for (int v = 0; v < 16; ++v) z[b][v] = 0.f;
 
   if constexpr (DT == 0) {
+    // Loads are unconditional (clamped in-bounds addresses) so that the
+    // prefetched group stays in flight while the current one is multiplied.
+    // Lanes past the last token read a valid row; their results are dropped.
+    // In a half-filled last K-step (h % 16 == 8) the upper-half lanes re-read
+    // the lower half: the packed R1 rows there are zero.
     constexpr int U = (RB == 1) ? 8 : (RB == 2 ? 4 : 2);  // K-steps per group
     const int KS = (a.h + 15) / 16;
-    const bf16x8* xrow = (const bf16x8*)((const uint16_t*)a.X + (size_t)(rowok ? n : tok0) * a.h + 8 * hf);
+    const long long row = rowok ? n : a.N - 1;
+    const uint16_t* xbase = (const uint16_t*)a.X + (size_t)row * a.h;
     const bf16x8* r1p = (const bf16x8*)a.R1p;
+    auto xaddr = [&](int s) {
+      const int c = (16 * s + 8 * hf < a.h) ? 16 * s + 8 * hf : 16 * s;
+      return (const bf16x8*)(xbase + c);
+    };
     bf16x8 xa[U], xb[U], ra[U][RB], rb[U][RB];
     auto load = [&](int g, bf16x8 (&xs)[U], bf16x8 (&rs)[U][RB]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int s = g * U + u;
-        bf16x8 xv;
+        xs[u] = __builtin_nontemporal_load(xaddr(s));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xv[e] = (bf16)0.f;
-        if (rowok && s < KS && 16 * s + 8 * hf < a.h) xv = __builtin_nontemporal_load(xrow + 2 * s);
-        xs[u] = xv;
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          bf16x8 rv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) rv[e] = (bf16)0.f;
-          if (s < KS) rv = r1p[((size_t)s * RB + b) * kWave + lane];
-          rs[u][b] = rv;
-        }
+        for (int b = 0; b < RB; ++b) rs[u][b] = r1p[((size_t)s * RB + b) * kWave + lane];
       }
     };
     auto compute = [&](const bf16x8 (&xs)[U], const bf16x8 (&rs)[U][RB]) {
@@ -98,15 +104,25 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_kernel(LowRankArgs a) {
 #pragma unroll
         for (int b = 0; b < RB; ++b) z[b] = mfma_bf16(rs[u][b], xs[u], z[b]);
     };
-    const int G = (KS + U - 1) / U;
-    load(0, xa, ra);
-    for (int g = 0; g < G; g += 2) {
-      if (g + 1 < G) load(g + 1, xb, rb);
-      compute(xa, ra);
-      if (g + 1 < G) {
-        if (g + 2 < G) load(g + 2, xa, ra);
+    const int G = KS / U;                       // full groups
+    if (G > 0) {
+      // No branch around a load: the group index is clamped instead (a
+      // re-load of the last group is harmless), which lets the compiler keep
+      // the next group in flight across the loop back-edge.
+      load(0, xa, ra);
+      int g = 0;
+      for (; g + 2 <= G; g += 2) {
+        load(g + 1, xb, rb);
+        compute(xa, ra);
+        load(min(g + 2, G - 1), xa, ra);
         compute(xb, rb);
       }
+      if (g < G) compute(xa, ra);
+    }
+    for (int s = G * U; s < KS; ++s) {          // remainder K-steps
+      const bf16x8 xv = __builtin_nontemporal_load(xaddr(s));
+#pragma unroll
+      for (int b = 0; b < RB; ++b) z[b] = mfma_bf16(r1p[((size_t)s * RB + b) * kWave + lane], xv, z[b]);
     }
   } else {
     const int KS = (a.h + 1) / 2;
@@ -122,7 +138,6 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_kernel(LowRankArgs a) {
   // ------------------------------------------------------------------ phase 2
   SweepState<KMAX, CAP> st;
   st.init(a.k);
-  const floatx16* biasp = (const floatx16*)a.biasp;        // [NT][2] x 16 floats
   if constexpr (DT == 0) {
     bf16x8 zh[R16], zl[R16];
 #pragma unroll
@@ -134,26 +149,58 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_kernel(LowRankArgs a) {
         zh[m][e] = hv;
         zl[m][e] = (bf16)(f - (float)hv);
       }
+    // ones in K-slots 0 and 1 of the lower lanes: A_bias x ones puts hi + lo
+    // of each expert's bias into every token column.
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (bf16)((!hi && e < 2) ? 1.f : 0.f);
     const bf16x8* r2p = (const bf16x8*)a.R2p;
-    floatx16 bc = biasp[hf];
-    bf16x8 a2[R16];
+    const uint32_t* bq = a.biasq;
+    struct Ops {
+      bf16x8 w[R16];
+      uint32_t b;
+    };
+    auto load_ops = [&](int t, Ops& o) {
+      const int tc = t < a.NT ? t : a.NT - 1;   // clamped: always a valid tile
 #pragma unroll
-    for (int m = 0; m < R16; ++m) a2[m] = r2p[(size_t)m * kWave + lane];
-    for (int t = 0; t < a.NT; ++t) {
-      floatx16 acc = bc;
+      for (int m = 0; m < R16; ++m) o.w[m] = r2p[((size_t)tc * R16 + m) * kWave + lane];
+      o.b = bq[(size_t)tc * kWave + lane];
+    };
+    auto logits = [&](const Ops& o) {
+      bf16x8 ab;
 #pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(a2[m], zh[m], acc);
+      for (int e = 0; e < 8; ++e) ab[e] = (bf16)0.f;
+      const uint32_t bw = o.b;
+      ab[0] = __builtin_bit_cast(bf16, (uint16_t)(bw & 0xffffu));
+      ab[1] = __builtin_bit_cast(bf16, (uint16_t)(bw >> 16));
+      floatx16 acc;
 #pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(a2[m], zl[m], acc);
-      if (t + 1 < a.NT) {
-        bc = biasp[2 * (t + 1) + hf];
+      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+      acc = mfma_bf16(ab, ones, acc);
 #pragma unroll
-        for (int m = 0; m < R16; ++m) a2[m] = r2p[((size_t)(t + 1) * R16 + m) * kWave + lane];
-      }
-      st.template tile<FULL>(acc, kTile * t + 4 * hf, lg, lane, hi, a.perm, a.k);
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(o.w[m], zh[m], acc);
+#pragma unroll
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(o.w[m], zl[m], acc);
+      return acc;
+    };
+    // Two tiles in flight: the MFMAs of tile t+1 are issued before the top-k
+    // work on tile t, and operands are fetched two tiles ahead.
+    Ops o0, o1;
+    load_ops(0, o0);
+    load_ops(1, o1);
+    floatx16 accA = logits(o0);
+    load_ops(2, o0);
+    for (int t = 0; t < a.NT; t += 2) {
+      floatx16 accB = logits(o1);
+      load_ops(t + 3, o1);
+      st.template tile<FULL>(accA, kTile * t + 4 * hf, lg, lane, hi, a.perm, a.k);
+      accA = logits(o0);                        // beyond the last tile: unused
+      load_ops(t + 4, o0);
+      if (t + 1 < a.NT) st.template tile<FULL>(accB, kTile * (t + 1) + 4 * hf, lg, lane, hi, a.perm, a.k);
     }
   } else {
     constexpr int KS2 = 8 * R16;
+    const floatx16* biasp = (const floatx16*)a.biasp;      // [NT][2] x 16 floats
     const float* r2p = (const float*)a.R2p;
     for (int t = 0; t < a.NT; ++t) {
       floatx16 acc = biasp[2 * t + hf];
@@ -164,60 +211,8 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_kernel(LowRankArgs a) {
     }
   }
 
-  // ------------------------------------------------------------------ merge
-  st.thr_p = partner_f32(st.L[KMAX - 1], hi);
-  st.thr = fmaxf(st.L[KMAX - 1], st.thr_p);
-  st.compact(lg, lane, a.perm, a.k);
-  const int cnt_p = (int)partner_u32((uint32_t)st.cnt, hi);
-  float lse = 0.f;
-  if (FULL) {
-    const float mp = partner_f32(st.m, hi), Zp = partner_f32(st.Z, hi);
-    const float mm = fmaxf(st.m, mp);
-    const float Zt = st.Z * __builtin_amdgcn_exp2f((st.m - mm) * kLog2e) +
-                     Zp * __builtin_amdgcn_exp2f((mp - mm) * kLog2e);
-    lse = mm + __builtin_amdgcn_logf(Zt) * kLn2;
-  }
-  if (hi || !rowok) return;
-  float V[KMAX];
-  int IX[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    V[j] = -__builtin_inff();
-    IX[j] = 0x7fffffff;
-  }
-  for (int c = 0; c < st.cnt; ++c) {
-    const float2 e = lg.base[c * kWave + lane];
-    ordered_insert<KMAX>(V, IX, e.x, a.perm[__float_as_int(e.y)]);
-  }
-  for (int c = 0; c < cnt_p; ++c) {
-    const float2 e = lg.base[c * kWave + lane + 32];
-    ordered_insert<KMAX>(V, IX, e.x, a.perm[__float_as_int(e.y)]);
-  }
-  float w[KMAX];
-  if (FULL) {
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) w[j] = __builtin_amdgcn_exp2f((V[j] - lse) * kLog2e);
-  } else {
-    float denom = 0.f;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      w[j] = (j < a.k) ? __builtin_amdgcn_exp2f((V[j] - V[0]) * kLog2e) : 0.f;
-      denom += w[j];
-    }
-    const float inv = 1.f / denom;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) w[j] *= inv;
-  }
-  const size_t o = (size_t)n * a.k;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < a.k) {
-      a.out_idx[o + j] = IX[j];
-      a.out_gate[o + j] = w[j];
-      if (a.out_logit) a.out_logit[o + j] = V[j];
-    }
-  }
-  if (FULL && a.out_lse) a.out_lse[n] = lse;
+  finish_tokens<KMAX, CAP, FULL>(st, lg, lane, hi, rowok, n, a.perm, a.k, a.out_idx, a.out_gate,
+                                 a.out_logit, a.out_lse);
 }
 
 }  // namespace more

@@ -35,7 +35,8 @@ struct PackArgs {
   // outputs (workspace)
   void* R1p;
   void* R2p;
-  float* biasp;       // [NT][2][16]
+  float* biasp;       // [NT][2][16] fp32, accumulator layout (fp32 kernels)
+  uint32_t* biasq;    // [NT][64] bf16 pairs (hi, lo) as an MFMA A operand (bf16 kernels)
   int* perm;          // [Mpad]
 };
 
@@ -103,7 +104,18 @@ __global__ __launch_bounds__(1024) void pack_kernel(PackArgs a) {
     if (slice == 0) {
       a.perm[pos] = (j < a.M) ? j : -1;
       const int hf = (i >> 2) & 1, v = 4 * (i >> 3) + (i & 3);
-      a.biasp[(t * 2 + hf) * 16 + v] = (j < a.M) ? (a.bias ? a.bias[j] : 0.f) : -__builtin_inff();
+      const float bv = (j < a.M) ? (a.bias ? a.bias[j] : 0.f) : -__builtin_inff();
+      a.biasp[(t * 2 + hf) * 16 + v] = bv;
+      if (a.biasq) {
+        // bias of row i as bf16 hi + lo in K-slots 0 and 1 of lane i (lanes 32..63
+        // carry zeros): one MFMA against a ones operand adds hi + lo to every token.
+        const bf16 bh = (bf16)bv;
+        const float rest = (j < a.M) ? bv - (float)bh : 0.f;
+        const bf16 bl = (bf16)rest;
+        a.biasq[(size_t)t * kWave + i] =
+            (uint32_t)__builtin_bit_cast(uint16_t, bh) | ((uint32_t)__builtin_bit_cast(uint16_t, bl) << 16);
+        a.biasq[(size_t)t * kWave + 32 + i] = 0u;
+      }
     }
     return;
   }

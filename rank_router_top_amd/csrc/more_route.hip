@@ -12,6 +12,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "more_route.h"
 #include "more_device.h"
 #include "more_pack.h"
@@ -31,12 +33,13 @@ size_t log_bytes(int kmax) { return (size_t)(2 * kmax + 8) * kWave * sizeof(floa
 
 struct Layout {
   int NT, Mpad, r16, rb, ks1, ks2, epl, esize;
-  size_t off_r1p, off_r2p, off_bias, off_perm, total;
+  size_t off_r1p, off_r2p, off_bias, off_biasq, off_perm, total;
 };
 
 // Workspace layout of one call.  All offsets are 256-byte aligned.
 bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, Layout* L) {
   L->NT = (int)((M + kTile - 1) / kTile);
+  L->NT += L->NT & 1;                       // even: the sweeps run tiles in pairs
   L->Mpad = L->NT * kTile;
   L->epl = (dt == MORE_DT_BF16) ? 8 : 1;
   L->esize = (dt == MORE_DT_BF16) ? 2 : 4;
@@ -51,6 +54,12 @@ bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, L
     L->rb = (L->r16 + 1) / 2;
     L->ks1 = (dt == MORE_DT_BF16) ? (int)((h + 15) / 16) : (int)((h + 1) / 2);
     L->ks2 = (dt == MORE_DT_BF16) ? L->r16 : 8 * L->r16;
+    if (dt == MORE_DT_BF16 && stream_supported(L->r16)) {
+      // the streaming kernel's ring consumes K-steps in batches of D: pad with
+      // zero weight rows so every batch is whole
+      const int D = stream_depth(L->r16);
+      L->ks1 = (L->ks1 + D - 1) / D * D;
+    }
   }
   size_t off = 0;
   L->off_r1p = off;
@@ -59,6 +68,8 @@ bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, L
   off += align_up((size_t)L->NT * L->ks2 * lane_bytes);
   L->off_bias = off;
   off += align_up((size_t)L->NT * 2 * 16 * sizeof(float));
+  L->off_biasq = off;
+  off += align_up((size_t)L->NT * kWave * sizeof(uint32_t));
   L->off_perm = off;
   off += align_up((size_t)L->Mpad * sizeof(int));
   L->total = off;
@@ -118,6 +129,7 @@ more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* 
   p.R1p = ws + L.off_r1p;
   p.R2p = ws + L.off_r2p;
   p.biasp = (float*)(ws + L.off_bias);
+  p.biasq = (uint32_t*)(ws + L.off_biasq);
   p.perm = (int*)(ws + L.off_perm);
   const int blocks = p.rank_blocks + p.r1_blocks;
   if (dt == MORE_DT_BF16)
@@ -203,14 +215,38 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   a.R1p = ws + L.off_r1p;
   a.R2p = ws + L.off_r2p;
   a.biasp = (const float*)(ws + L.off_bias);
+  a.biasq = (const uint32_t*)(ws + L.off_biasq);
   a.perm = (const int*)(ws + L.off_perm);
   a.out_idx = topk_idx;
   a.out_gate = topk_gate;
   a.out_logit = topk_logit;
   a.out_lse = full ? lse : nullptr;
+  const size_t shmem = (size_t)waves * log_bytes(kmax);
+  if (dt == MORE_DT_BF16 && stream_supported(L.r16)) {
+    // Persistent grid: as many waves as fit on the device at once, each owning
+    // an equal number of 32-token blocks.
+    stream_fn fn = pick_stream(full, kmax, L.r16);
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fn, 64 * waves, shmem) !=
+            hipSuccess)
+      return MORE_ERR_HIP;
+    StreamArgs sa;
+    sa.base = a;
+    const int64_t nb = (N + kTile - 1) / kTile;
+    if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
+    sa.NB = (int)nb;
+    const int64_t slots = std::max<int64_t>(1, (int64_t)cus * std::max(per_cu, 1) * waves);
+    const int64_t per_wave = (nb + slots - 1) / slots;
+    sa.G = (int)((nb + per_wave - 1) / per_wave);
+    sa.KSP = L.ks1;
+    const dim3 grid((unsigned)((sa.G + waves - 1) / waves));
+    hipLaunchKernelGGL(fn, grid, dim3(64 * waves), shmem, (hipStream_t)stream, sa);
+    return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+  }
   const int64_t per_block = (int64_t)waves * kTile;
   const dim3 grid((unsigned)((N + per_block - 1) / per_block));
-  const size_t shmem = (size_t)waves * log_bytes(kmax);
   hipLaunchKernelGGL(pick_lowrank(dt, full, kmax, L.r16), grid, dim3(64 * waves), shmem,
                      (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
