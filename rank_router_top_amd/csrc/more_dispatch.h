@@ -4,6 +4,7 @@
 #include "more_lowrank.h"
 #include "more_fullrank.h"
 #include "more_stream.h"
+#include "more_lock.h"
 
 namespace more {
 
@@ -21,6 +22,15 @@ constexpr int stream_depth(int r16) { return r16 <= 2 ? 8 : 4; }
 // The streaming kernel covers bf16 storage with r <= 64.
 constexpr bool stream_supported(int r16) { return r16 <= 4; }
 stream_fn pick_stream(bool full, int kmax, int r16);
+
+// Workgroup-lockstep kernel: bf16, k <= 8, r <= 64, M <= 65536 (16-bit positions).
+typedef void (*lock_fn)(LockArgs);
+constexpr int kLockKPBM = 4;   // K-steps per batch (max)
+constexpr int kLockTPBM = 4;   // expert tiles per batch (max)
+constexpr bool lock_supported(int kmax, int r16, long long mpad) {
+  return kmax <= 8 && r16 <= 4 && mpad <= 65536;
+}
+lock_fn pick_lock(bool full, int kmax, int r16, size_t* lds_bytes);
 
 lowrank_fn pick_lowrank_bf16_topk(int kmax, int r16);
 lowrank_fn pick_lowrank_bf16_full(int kmax, int r16);

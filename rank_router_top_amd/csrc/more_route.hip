@@ -69,7 +69,8 @@ bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, L
   L->off_bias = off;
   off += align_up((size_t)L->NT * 2 * 16 * sizeof(float));
   L->off_biasq = off;
-  off += align_up((size_t)L->NT * kWave * sizeof(uint32_t));
+  // rounded up to whole groups of 4 tiles: the lockstep kernel stages bias 1 KiB at a time
+  off += align_up((size_t)((L->NT + 3) / 4 * 4) * kWave * sizeof(uint32_t));
   L->off_perm = off;
   off += align_up((size_t)L->Mpad * sizeof(int));
   L->total = off;
@@ -222,6 +223,29 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   a.out_logit = topk_logit;
   a.out_lse = full ? lse : nullptr;
   const size_t shmem = (size_t)waves * log_bytes(kmax);
+  if (dt == MORE_DT_BF16 && lock_supported(kmax, L.r16, L.Mpad)) {
+    // Workgroup-lockstep kernel, one 8-wave workgroup per CU, persistent.
+    size_t lds = 0;
+    lock_fn fn = pick_lock(full, kmax, L.r16, &lds);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+            hipSuccess)
+      return MORE_ERR_HIP;
+    LockArgs la;
+    la.base = a;
+    const int64_t nb = (N + kTile - 1) / kTile;
+    if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
+    la.NB = (int)nb;
+    const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kLockWaves - 1) / kLockWaves));
+    la.G = (int)(wgs * kLockWaves);
+    la.NI = (int)((nb + la.G - 1) / la.G);
+    la.KS = (int)((h + 15) / 16);
+    la.NBATCH = std::max((L.NT + kLockTPBM - 1) / kLockTPBM, (la.KS + kLockKPBM - 1) / kLockKPBM);
+    hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(64 * kLockWaves), lds, (hipStream_t)stream, la);
+    return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+  }
   if (dt == MORE_DT_BF16 && stream_supported(L.r16)) {
     // Persistent grid: as many waves as fit on the device at once, each owning
     // an equal number of 32-token blocks.
