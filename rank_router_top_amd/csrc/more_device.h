@@ -177,6 +177,55 @@ struct SweepState {
   }
 };
 
+// Branch-free variant of SweepState::tile used by the producer/consumer
+// kernel: inside a 4-value group that holds a candidate in some lane, every
+// value goes through the v_med3 list unconditionally (a value below the list's
+// k-th leaves it unchanged, and one between the own k-th and the effective
+// threshold only raises the own k-th, which stays a valid lower bound), and is
+// written to log slot cnt unconditionally; cnt advances only for values that
+// reach the threshold, so rejected writes are overwritten later.  Only the
+// tile and group tests branch.
+template <int KMAX, int CAP, bool FULL>
+__device__ __forceinline__ void tile_bf(SweepState<KMAX, CAP>& st, const floatx16& acc, int pos_base,
+                                        LogRef lg, int lane, bool hi_half, const int* __restrict__ perm,
+                                        int k) {
+  float g[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    g[q] = fmaxf(fmaxf(acc[4 * q], acc[4 * q + 1]), fmaxf(acc[4 * q + 2], acc[4 * q + 3]));
+  const float tmax = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
+  if (FULL) {
+    const float mn = fmaxf(st.m, tmax);
+    const float mb = mn * kLog2e;
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kLog2e, -mb));
+    st.Z = st.Z * __builtin_amdgcn_exp2f((st.m - mn) * kLog2e) + s;
+    st.m = mn;
+  }
+  st.thr_p = partner_f32(st.L[KMAX - 1], hi_half);
+  st.thr = fmaxf(st.L[KMAX - 1], st.thr_p);
+  if (any_lane(tmax >= st.thr)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (any_lane(g[q] >= st.thr)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = acc[4 * q + e];
+          const bool take = x >= st.thr;
+          lg.base[st.cnt * kWave + lane] = make_float2(x, __int_as_float(pos_base + 8 * q + e));
+          st.cnt += take ? 1 : 0;
+#pragma unroll
+          for (int j = KMAX - 1; j >= 1; --j) st.L[j] = __builtin_amdgcn_fmed3f(st.L[j - 1], st.L[j], x);
+          st.L[0] = fmaxf(st.L[0], x);
+          st.thr = fmaxf(st.L[KMAX - 1], st.thr_p);
+        }
+        if (any_lane(st.cnt > CAP - 4)) st.compact(lg, lane, perm, k);
+      }
+    }
+  }
+}
+
 // Tie-aware sorted insertion used once per token at the end: order is
 // (value descending, original expert index ascending).
 template <int KMAX>

@@ -5,6 +5,7 @@
 #include "more_fullrank.h"
 #include "more_stream.h"
 #include "more_lock.h"
+#include "more_pc.h"
 
 namespace more {
 
@@ -31,6 +32,26 @@ constexpr bool lock_supported(int kmax, int r16, long long mpad) {
   return kmax <= 8 && r16 <= 4 && mpad <= 65536;
 }
 lock_fn pick_lock(bool full, int kmax, int r16, size_t* lds_bytes);
+
+// Producer/consumer kernel: bf16, k <= 8, r <= 64, M <= 65536, LDS within 160 KiB.
+typedef void (*pc_fn)(PcArgs);
+// Producer ring depth (K-steps in flight): 8 for r <= 32, 4 for r = 64 and for
+// the tail instances (h % 32 != 0 or padded K-steps; small odd shapes only).
+constexpr int pc_depth(int r16, bool tail) { return (tail || r16 > 2) ? 4 : 8; }
+// K-steps of the producer and whether the tail instance is needed.
+inline void pc_ksteps(long long h, int r16, int* ksp, bool* tail) {
+  const long long ks = (h + 31) / 32;
+  *tail = (h % 32 != 0) || (ks % pc_depth(r16, false) != 0);
+  const int D = pc_depth(r16, *tail);
+  *ksp = (int)((ks + D - 1) / D * D);
+}
+constexpr long long kLdsBytes = 160 * 1024;
+constexpr bool pc_shape_ok(int kmax, int r16, long long mpad) {
+  return kmax <= 8 && r16 <= 4 && mpad <= 65536;
+}
+// Dynamic LDS of the instance for (kmax, r16, mpad); 0 if no instance exists.
+size_t pc_lds_bytes(int kmax, int r16, long long mpad);
+pc_fn pick_pc(bool full, int kmax, int r16, bool tail);
 
 lowrank_fn pick_lowrank_bf16_topk(int kmax, int r16);
 lowrank_fn pick_lowrank_bf16_full(int kmax, int r16);

@@ -32,8 +32,11 @@ struct PackArgs {
   int natural_k;      // 1: second-product K rows in memory order (full rank: the X operand)
   int rank_blocks;    // blocks computing the sweep order (64 experts each)
   int r1_blocks;      // blocks packing R1
+  int ksq, r16;       // producer layout of R1: 32-column K-steps (padded) and 16-rank blocks
+  int r1q_blocks;     // blocks packing R1q (0: not wanted)
   // outputs (workspace)
   void* R1p;
+  void* R1q;          // [ksq][r16][64][8] bf16, A operand of v_mfma_f32_16x16x32_bf16 (R1^T block)
   void* R2p;
   float* biasp;       // [NT][2][16] fp32, accumulator layout (fp32 kernels)
   uint32_t* biasq;    // [NT][64] bf16 pairs (hi, lo) as an MFMA A operand (bf16 kernels)
@@ -115,6 +118,26 @@ __global__ __launch_bounds__(1024) void pack_kernel(PackArgs a) {
         a.biasq[(size_t)t * kWave + i] =
             (uint32_t)__builtin_bit_cast(uint16_t, bh) | ((uint32_t)__builtin_bit_cast(uint16_t, bl) << 16);
         a.biasq[(size_t)t * kWave + 32 + i] = 0u;
+      }
+    }
+    return;
+  }
+  if ((int)blockIdx.x >= a.rank_blocks + a.r1_blocks) {
+    // ---- R1q (bf16, low rank): entry (s, rb, lane) holds rows 32s + 8(lane/16) .. +7
+    // of R1, column 16rb + lane%16 -- lane l of the A operand is row l%16 of the
+    // 16 x 32 block R1^T[16rb.., 32s..], K slots 8(l/16) .. +7.
+    if constexpr (DT == 0) {
+      const int gq = ((int)blockIdx.x - a.rank_blocks - a.r1_blocks) * 1024 + tid;
+      if (gq >= a.ksq * a.r16 * kWave) return;
+      const int lane = gq % kWave, srb = gq / kWave;
+      const int rbk = srb % a.r16, s = srb / a.r16;
+      const int col = 16 * rbk + (lane & 15);
+      const uint16_t* A = (const uint16_t*)a.R1;
+      uint16_t* Aq = (uint16_t*)a.R1q;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int hrow = 32 * s + 8 * (lane >> 4) + e;
+        Aq[(size_t)gq * 8 + e] = (hrow < a.h && col < a.r) ? A[(size_t)hrow * a.r + col] : (uint16_t)0;
       }
     }
     return;

@@ -1,0 +1,340 @@
+// more_pc.h -- producer/consumer form of the fused low-rank router (bf16
+// storage, k <= 8, r <= 64, M <= 65536) for gfx950.
+//
+// Method: "MoRE: Scaling mixture of experts with hardware-aware low-rank
+// routing", App. F.1 Algorithm 1: per block of tokens, phase 1 computes the
+// rank-r intermediate z = X-block times the down-projection on chip, phase 2
+// sweeps the experts once with a running top-k; only N x k results reach HBM.
+//
+// The two phases stress different units: phase 1 is a pure HBM stream (all of
+// X, ~4 KiB per token at h = 2048) with a little MFMA work, phase 2 is MFMA +
+// VALU work on L2-resident weights.  When one wave interleaves both, the HBM
+// loads sit in the same in-order vector-memory counter as the short-latency
+// weight loads, and either the stream stalls or the sweep waits on HBM.  Here
+// the two phases run on different waves of one persistent workgroup per CU:
+//
+//   4 producer waves (one per SIMD): stream X through a ring of D register
+//     slots with v_mfma_f32_16x16x32_bf16, whose B operand is exactly what a
+//     16-byte load of 16 rows x 64 bytes delivers (no LDS transpose); at the
+//     end of a 32-token block they split z into bf16 hi + lo parts and write
+//     them into the LDS slot of the consumer that owns the block;
+//   8 consumer waves: read z from their slot (then free it), and sweep all
+//     expert tiles with v_mfma_f32_32x32x16_bf16: logits^T = R2^T z + bias
+//     (bias enters as the fp32 accumulator input, staged once in LDS), with
+//     the two-pass exact top-k of more_twopass.h.
+//
+// Hand-off: per consumer, two LDS counters (blocks produced / blocks read).
+// Each wait is a bounded spin: if a counter does not move within spin_limit
+// polls (a protocol error, never expected), the wave sets an abort word that
+// every other wave checks at its next wait, so the kernel always terminates.
+//
+// Block schedule inside workgroup g: local blocks i = 0, 1, ... are global
+// blocks g + i*G; producer p streams i = p, p+4, ...; consumer c sweeps
+// i = c, c+8, ... (consumers c and c+4 are both fed by producer c%4).
+#pragma once
+#include "more_device.h"
+#include "more_lowrank.h"
+#include "more_lock.h"
+#include "more_twopass.h"
+
+namespace more {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kPcProd = 4;                     // producer waves per workgroup
+constexpr int kPcCons = 8;                     // consumer waves per workgroup
+constexpr int kPcWaves = kPcProd + kPcCons;
+constexpr int kBufWord3 = 0x00020000;          // raw buffer, 32-bit data format
+constexpr int kOob = 0x40000000;               // offset past any descriptor range: loads 0
+
+struct PcArgs {
+  LowRankArgs base;    // X, N, h, NT (multiple of 4), k, R2p, biasp, perm, outputs
+  const void* R1q;     // [KSP][R16][64][8] bf16: A operand (R1^T block) of each K-step
+  int NB;              // 32-token blocks
+  int G;               // workgroups
+  int KSP;             // 32-column K-steps, padded to a multiple of D (zero R1 rows)
+  int spin_limit;      // polls before a wait gives up
+};
+
+// LDS map (bytes): flags | z slots | logs | bias
+template <int KMAX, int R16>
+struct PcLds {
+  static constexpr int CAP = Cap<KMAX>::value;
+  static constexpr int kFlags = 128;   // int full[8], free[8], abort
+  static constexpr int kZ = kFlags;    // [cons][hi, lo][R16][64 lanes][16 B]
+  static constexpr int kZBytes = kPcCons * 2 * R16 * 1024;
+  static constexpr int kLog = kZ + kZBytes;                           // [cons][CAP][64] (value, position)
+  static constexpr int kBias = kLog + kPcCons * CAP * kWave * 8;      // [NT][2][16] f32
+  static constexpr size_t bytes(long long mpad) { return (size_t)kBias + (size_t)mpad * 4; }
+};
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufWord3);
+}
+// AUX = 2: non-temporal (streamed once); 0: default caching.
+template <int AUX = 0>
+__device__ __forceinline__ bf16x8 buf_load(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+__device__ __forceinline__ void lds_drain() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// The hand-off counters are addressed explicitly in the LDS address space: a
+// volatile access through a generic pointer becomes a FLAT instruction, which
+// also counts against the vector-memory counter, and waiting for it would
+// drain every load in flight (the X ring of a producer, the operand ring of a
+// consumer).
+typedef __attribute__((address_space(3))) int lds_i32;
+typedef volatile lds_i32* flag_ptr;
+__device__ __forceinline__ flag_ptr pc_flags(char* lds) { return (flag_ptr)(lds_i32*)lds; }
+
+// Bounded wait until *f >= need.  Returns false (and raises abort) on timeout
+// or when another wave has aborted.
+__device__ __forceinline__ bool pc_wait(flag_ptr f, int need, flag_ptr abort_word, int limit) {
+  for (int it = 0;; ++it) {
+    if (__builtin_amdgcn_readfirstlane(*f) >= need) break;
+    if (__builtin_amdgcn_readfirstlane(*abort_word) != 0 || it >= limit) {
+      *abort_word = 1;
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");   // later LDS reads stay after the poll
+  return true;
+}
+
+// ------------------------------------------------------------------ producer
+// TAIL: h is not a multiple of 32, or the K-steps are padded to a whole ring;
+// then the columns past h are replaced by out-of-range offsets (zeros).
+// Otherwise every K-step lies inside the row and its column offset is a
+// scalar, so the X loads need no per-lane arithmetic at all.
+template <int KMAX, int R16, int D, bool TAIL>
+__device__ __forceinline__ void pc_produce(const PcArgs& pa, char* lds, int p, int lane, int nbw) {
+  typedef PcLds<KMAX, R16> L;
+  const LowRankArgs& a = pa.base;
+  const int nj = (nbw - p + kPcProd - 1) / kPcProd;   // blocks of this producer
+  if (nj <= 0) return;
+  flag_ptr full = pc_flags(lds);
+  flag_ptr freed = full + kPcCons;
+  flag_ptr abort_word = full + 2 * kPcCons;
+  const int l16 = lane & 15, q4 = lane >> 4;
+  const int rowbytes = a.h * 2;
+  const int vrow0 = l16 * rowbytes, vrow1 = (16 + l16) * rowbytes;
+  const rsrc_t r1d = make_rsrc(pa.R1q, pa.KSP * R16 * 1024);
+  const int NBAT = pa.KSP / D;
+
+  // rows of block jj (fewer at the tail of X; none past the last block)
+  auto xbase = [&](int jj) -> const char* {
+    const long long b = (long long)blockIdx.x + (long long)(p + kPcProd * jj) * pa.G;
+    return (const char*)a.X + (size_t)b * kTile * rowbytes;
+  };
+  auto xbytes = [&](int jj) -> int {
+    if (jj >= nj) return 0;
+    const long long b = (long long)blockIdx.x + (long long)(p + kPcProd * jj) * pa.G;
+    const long long rows = a.N - b * kTile;
+    return (int)((rows < kTile ? rows : kTile) * rowbytes);
+  };
+
+  bf16x8 xr[D][2], rr[D][R16];
+  const int vx0 = vrow0 + 16 * q4, vx1 = vrow1 + 16 * q4;
+  auto issue = [&](int u, rsrc_t xd, int s) {
+    if constexpr (TAIL) {
+      const int c2 = 64 * s + 16 * q4;   // byte column of this lane's 8 elements
+      const bool ok = c2 < rowbytes;
+      xr[u][0] = buf_load<2>(xd, ok ? vrow0 + c2 : kOob, 0);
+      xr[u][1] = buf_load<2>(xd, ok ? vrow1 + c2 : kOob, 0);
+    } else {
+      xr[u][0] = buf_load<2>(xd, vx0, 64 * s);
+      xr[u][1] = buf_load<2>(xd, vx1, 64 * s);
+    }
+#pragma unroll
+    for (int rb = 0; rb < R16; ++rb) rr[u][rb] = buf_load(r1d, lane * 16 + rb * 1024, s * R16 * 1024);
+  };
+
+  const char* cbase = xbase(0);
+  int cbytes = xbytes(0);
+  const char* nbase = xbase(1);
+  int nbytes = xbytes(1);
+  {
+    const rsrc_t xd = make_rsrc(cbase, cbytes);
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      issue(u, xd, u);
+      __builtin_amdgcn_sched_barrier(0);   // slot order here too (the loop's wait counts assume it)
+    }
+  }
+  for (int jj = 0; jj < nj; ++jj) {
+    floatx4 acc[2][R16];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int rb = 0; rb < R16; ++rb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[g][rb][v] = 0.f;
+    for (int sb = 0; sb < NBAT; ++sb) {
+      const bool last = sb == NBAT - 1;   // refill with the next block's first K-steps
+      const rsrc_t xd = make_rsrc(last ? nbase : cbase, last ? nbytes : cbytes);
+      const int s0 = last ? 0 : (sb + 1) * D;
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int rb = 0; rb < R16; ++rb)
+            acc[g][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rr[u][rb], xr[u][g], acc[g][rb], 0, 0, 0);
+        issue(u, xd, s0 + u);
+        // keep slot order: the MFMAs of slot u wait only for slot u's loads
+        // (D-1 newer slots stay in flight); without the barrier the scheduler
+        // groups all MFMAs of a batch ahead of all its loads, which makes every
+        // batch wait for the whole ring
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // acc[g][rb][v] = z[token 16g + l16][rank 16rb + 4q4 + v]: hand it to the consumer
+    const int i = p + kPcProd * jj;
+    const int cc = i % kPcCons, jc = i / kPcCons;
+    if (!pc_wait(freed + cc, jc, abort_word, pa.spin_limit)) return;
+    char* slot = lds + L::kZ + cc * 2 * R16 * 1024;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      // consumer lane 16g + l16 + 32(q4&1), elements 4(q4>>1) .. +3 of K-step rb
+      const int off = (16 * g + l16 + 32 * (q4 & 1)) * 16 + 8 * (q4 >> 1);
+#pragma unroll
+      for (int rb = 0; rb < R16; ++rb) {
+        uint32_t hv[2], lv[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float f0 = acc[g][rb][2 * h2], f1 = acc[g][rb][2 * h2 + 1];
+          const bf16 a0 = (bf16)f0, a1 = (bf16)f1;
+          const bf16 b0 = (bf16)(f0 - (float)a0), b1 = (bf16)(f1 - (float)a1);
+          hv[h2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+          lv[h2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        }
+        *(uint2*)(slot + rb * 1024 + off) = make_uint2(hv[0], hv[1]);
+        *(uint2*)(slot + (R16 + rb) * 1024 + off) = make_uint2(lv[0], lv[1]);
+      }
+    }
+    lds_drain();
+    full[cc] = jc + 1;
+    cbase = nbase;
+    cbytes = nbytes;
+    nbase = xbase(jj + 2);
+    nbytes = xbytes(jj + 2);
+  }
+}
+
+// ------------------------------------------------------------------ consumer
+template <int KMAX, bool FULL, int R16>
+__device__ __forceinline__ void pc_consume(const PcArgs& pa, char* lds, int c, int lane, int nbw) {
+  typedef PcLds<KMAX, R16> L;
+  constexpr int CAP = L::CAP;
+  const LowRankArgs& a = pa.base;
+  const int nj = (nbw - c + kPcCons - 1) / kPcCons;
+  if (nj <= 0) return;
+  flag_ptr full = pc_flags(lds);
+  flag_ptr freed = full + kPcCons;
+  flag_ptr abort_word = full + 2 * kPcCons;
+  const bool hi = lane >= 32;
+  const int hf = hi ? 1 : 0;
+  LogRef lg{(float2*)(lds + L::kLog) + c * CAP * kWave};
+  const float* lb = (const float*)(lds + L::kBias);
+  const char* slot = lds + L::kZ + c * 2 * R16 * 1024;
+  const int NT = a.NT;
+  const rsrc_t r2d = make_rsrc(a.R2p, NT * R16 * 1024);
+
+  struct Ops {
+    bf16x8 w[R16];
+  };
+  auto load_ops = [&](int t, Ops& o) {
+#pragma unroll
+    for (int m = 0; m < R16; ++m) o.w[m] = buf_load(r2d, lane * 16 + m * 1024, t * R16 * 1024);
+  };
+  bf16x8 zh[R16], zl[R16];
+  // bias of tile t in accumulator layout (read one tile ahead of its use)
+  auto bias = [&](int t) -> floatx16 { return *(const floatx16*)(lb + (2 * t + hf) * 16); };
+  auto logits = [&](const Ops& o, const floatx16& b) -> floatx16 {
+    floatx16 acc = b;
+#pragma unroll
+    for (int m = 0; m < R16; ++m) acc = mfma_bf16(o.w[m], zh[m], acc);
+#pragma unroll
+    for (int m = 0; m < R16; ++m) acc = mfma_bf16(o.w[m], zl[m], acc);
+    return acc;
+  };
+  auto wrap = [&](int t) { return t >= NT ? t - NT : t; };   // t < 2 NT
+
+  // Software pipeline over the expert tiles (NT is a multiple of 4): at step t
+  // the VALU works on tile t while the MFMAs of tile t+1 run; the weight
+  // operands of tile t+1 were requested at step t-4 (a 4-slot register ring,
+  // so three newer requests may still be in flight: the wait never reaches
+  // back to a recent L2 request) and its bias (LDS) at step t-2.  The ring
+  // wraps into the next pass's first tiles at the end of a pass.  Each block
+  // is swept twice (more_twopass.h): pass 1 finds the token threshold, pass 2
+  // logs the logits that reach it.
+  Ops o[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) load_ops(u, o[u]);
+  floatx16 bq[2];
+  bq[0] = bias(0);
+  bq[1] = bias(1);
+  // one pass over all tiles; per_tile(acc, t) sees the logits of tile t
+  auto sweep = [&](auto&& per_tile) {
+    floatx16 acc[2];
+    acc[0] = logits(o[0], bq[0]);
+    load_ops(wrap(4), o[0]);
+    bq[0] = bias(2);
+    for (int t0 = 0; t0 < NT; t0 += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + u;
+        const bool last = t == NT - 1;   // then tile t+1 is the next pass's tile 0 (discarded)
+        acc[(u + 1) & 1] = logits(o[(u + 1) & 3], bq[(u + 1) & 1]);
+        bq[(u + 1) & 1] = bias(last ? 0 : wrap(t + 3));
+        load_ops(last ? 0 : wrap(t + 5), o[(u + 1) & 3]);
+        per_tile(acc[u & 1], t);
+        __builtin_amdgcn_sched_barrier(0);   // keep the step order (wait counts rely on it)
+      }
+    }
+  };
+  TwoPassState<KMAX> st;
+  for (int jj = 0; jj < nj; ++jj) {
+    if (!pc_wait(full + c, jj + 1, abort_word, pa.spin_limit)) return;
+#pragma unroll
+    for (int m = 0; m < R16; ++m) {
+      zh[m] = *(const bf16x8*)(slot + m * 1024 + lane * 16);
+      zl[m] = *(const bf16x8*)(slot + (R16 + m) * 1024 + lane * 16);
+    }
+    lds_drain();
+    freed[c] = jj + 1;
+    st.init(a.k);
+    sweep([&](const floatx16& acc, int) { tp_pass1_tile<KMAX, FULL>(st, acc); });
+    tp_threshold<KMAX>(st, hi, a.k);
+    sweep([&](const floatx16& acc, int t) {
+      tp_pass2_tile<KMAX, CAP>(st, acc, kTile * t + 4 * hf, lg, lane, a.perm, a.k);
+    });
+    const long long b = (long long)blockIdx.x + (long long)(c + kPcCons * jj) * pa.G;
+    const long long n = b * kTile + (lane & 31);
+    tp_finish<KMAX, FULL>(st, lg, lane, hi, n < a.N, n, a.perm, a.k, a.out_idx, a.out_gate, a.out_logit,
+                          a.out_lse);
+  }
+}
+
+template <int KMAX, bool FULL, int R16, int D, bool TAIL>
+__global__ __launch_bounds__(64 * kPcWaves) void pc_kernel(PcArgs pa) {
+  typedef PcLds<KMAX, R16> L;
+  extern __shared__ __align__(16) char pc_lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // stage the bias (accumulator layout, -inf on padding rows); clear the counters
+  const int n4 = pa.base.NT * 8;
+  const float4* src = (const float4*)pa.base.biasp;
+  float4* dst = (float4*)(pc_lds + L::kBias);
+  for (int i = threadIdx.x; i < n4; i += 64 * kPcWaves) dst[i] = src[i];
+  if (threadIdx.x < L::kFlags / 4) ((int*)pc_lds)[threadIdx.x] = 0;
+  __syncthreads();
+  const int nbw = (pa.NB - (int)blockIdx.x + pa.G - 1) / pa.G;   // blocks of this workgroup
+  if (wave < kPcProd)
+    pc_produce<KMAX, R16, D, TAIL>(pa, pc_lds, wave, lane, nbw);
+  else
+    pc_consume<KMAX, FULL, R16>(pa, pc_lds, wave - kPcProd, lane, nbw);
+}
+
+}  // namespace more

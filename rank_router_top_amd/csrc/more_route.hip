@@ -32,18 +32,19 @@ int waves_for(int kmax) { return waves_for_kmax(kmax); }
 size_t log_bytes(int kmax) { return (size_t)(2 * kmax + 8) * kWave * sizeof(float2); }
 
 struct Layout {
-  int NT, Mpad, r16, rb, ks1, ks2, epl, esize;
-  size_t off_r1p, off_r2p, off_bias, off_biasq, off_perm, total;
+  int NT, Mpad, r16, rb, ks1, ks2, ksq, epl, esize;
+  size_t off_r1p, off_r2p, off_bias, off_biasq, off_perm, off_r1q, total;
 };
 
 // Workspace layout of one call.  All offsets are 256-byte aligned.
 bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, Layout* L) {
   L->NT = (int)((M + kTile - 1) / kTile);
-  L->NT += L->NT & 1;                       // even: the sweeps run tiles in pairs
+  L->NT = (L->NT + 3) / 4 * 4;              // whole groups of 4 tiles (sweep pipelines)
   L->Mpad = L->NT * kTile;
   L->epl = (dt == MORE_DT_BF16) ? 8 : 1;
   L->esize = (dt == MORE_DT_BF16) ? 2 : 4;
   const size_t lane_bytes = (size_t)kWave * L->epl * L->esize;   // one K-step operand
+  L->ksq = 0;
   if (fullrank) {
     L->r16 = 0;
     L->rb = 0;
@@ -60,6 +61,11 @@ bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, L
       const int D = stream_depth(L->r16);
       L->ks1 = (L->ks1 + D - 1) / D * D;
     }
+    if (dt == MORE_DT_BF16 && L->r16 <= 4) {
+      // producer/consumer kernel: 32-column K-steps in whole batches of its ring depth
+      bool tail = false;
+      pc_ksteps(h, L->r16, &L->ksq, &tail);
+    }
   }
   size_t off = 0;
   L->off_r1p = off;
@@ -73,6 +79,8 @@ bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, L
   off += align_up((size_t)((L->NT + 3) / 4 * 4) * kWave * sizeof(uint32_t));
   L->off_perm = off;
   off += align_up((size_t)L->Mpad * sizeof(int));
+  L->off_r1q = off;
+  off += align_up((size_t)L->ksq * L->r16 * 1024);
   L->total = off;
   return true;
 }
@@ -127,12 +135,16 @@ more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* 
   p.rank_blocks = (L.Mpad + 63) / 64;
   const int r1_total = L.ks1 * L.rb * kWave;
   p.r1_blocks = fullrank ? 0 : (r1_total + 1023) / 1024;
+  p.ksq = L.ksq;
+  p.r16 = L.r16;
+  p.r1q_blocks = (L.ksq * L.r16 * kWave + 1023) / 1024;
+  p.R1q = ws + L.off_r1q;
   p.R1p = ws + L.off_r1p;
   p.R2p = ws + L.off_r2p;
   p.biasp = (float*)(ws + L.off_bias);
   p.biasq = (uint32_t*)(ws + L.off_biasq);
   p.perm = (int*)(ws + L.off_perm);
-  const int blocks = p.rank_blocks + p.r1_blocks;
+  const int blocks = p.rank_blocks + p.r1_blocks + p.r1q_blocks;
   if (dt == MORE_DT_BF16)
     hipLaunchKernelGGL(pack_kernel<0>, dim3(blocks), dim3(1024), 0, stream, p);
   else
@@ -223,6 +235,31 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   a.out_logit = topk_logit;
   a.out_lse = full ? lse : nullptr;
   const size_t shmem = (size_t)waves * log_bytes(kmax);
+  const size_t pc_lds = (dt == MORE_DT_BF16 && L.ksq > 0) ? pc_lds_bytes(kmax, L.r16, L.Mpad) : 0;
+  if (pc_lds > 0 && (long long)pc_lds <= kLdsBytes) {
+    // Producer/consumer kernel: one 12-wave workgroup per CU, persistent.
+    int ksp = 0;
+    bool tail = false;
+    pc_ksteps(h, L.r16, &ksp, &tail);
+    pc_fn fn = pick_pc(full, kmax, L.r16, tail);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pc_lds) !=
+            hipSuccess)
+      return MORE_ERR_HIP;
+    PcArgs pa;
+    pa.base = a;
+    const int64_t nb = (N + kTile - 1) / kTile;
+    if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
+    pa.NB = (int)nb;
+    pa.G = (int)std::max<int64_t>(1, std::min<int64_t>(cus, nb));
+    pa.KSP = L.ksq;
+    pa.R1q = ws + L.off_r1q;
+    pa.spin_limit = 1 << 22;
+    hipLaunchKernelGGL(fn, dim3((unsigned)pa.G), dim3(64 * kPcWaves), pc_lds, (hipStream_t)stream, pa);
+    return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+  }
   if (dt == MORE_DT_BF16 && lock_supported(kmax, L.r16, L.Mpad)) {
     // Workgroup-lockstep kernel, one 8-wave workgroup per CU, persistent.
     size_t lds = 0;
