@@ -6,6 +6,7 @@
 #include "more_stream.h"
 #include "more_lock.h"
 #include "more_pc.h"
+#include "more_slice.h"
 
 namespace more {
 
@@ -52,6 +53,15 @@ constexpr bool pc_shape_ok(int kmax, int r16, long long mpad) {
 // Dynamic LDS of the instance for (kmax, r16, mpad); 0 if no instance exists.
 size_t pc_lds_bytes(int kmax, int r16, long long mpad);
 pc_fn pick_pc(bool full, int kmax, int r16, bool tail);
+
+// Expert-slice kernel: bf16, r in {16, 32}, M = 4096 (128 tiles), k <= 8.
+// LDS bytes (0: no instance) and instance.
+typedef void (*slice_fn)(SlArgs);
+constexpr bool slice_shape_ok(int kmax, int r16, long long mpad) {
+  return kmax <= kSlK && (r16 == 1 || r16 == 2) && mpad == (long long)kSlNT * kTile;
+}
+size_t slice_lds_bytes(bool full, int r16);
+slice_fn pick_slice(bool full, int r16, bool tail);
 
 lowrank_fn pick_lowrank_bf16_topk(int kmax, int r16);
 lowrank_fn pick_lowrank_bf16_full(int kmax, int r16);

@@ -46,6 +46,7 @@ constexpr int kPcCons = 8;                     // consumer waves per workgroup
 constexpr int kPcWaves = kPcProd + kPcCons;
 constexpr int kBufWord3 = 0x00020000;          // raw buffer, 32-bit data format
 constexpr int kOob = 0x40000000;               // offset past any descriptor range: loads 0
+constexpr int kPcZOff = 128;                   // LDS: hand-off counters, then the z slots
 
 struct PcArgs {
   LowRankArgs base;    // X, N, h, NT (multiple of 4), k, R2p, biasp, perm, outputs
@@ -60,8 +61,8 @@ struct PcArgs {
 template <int KMAX, int R16>
 struct PcLds {
   static constexpr int CAP = Cap<KMAX>::value;
-  static constexpr int kFlags = 128;   // int full[8], free[8], abort
-  static constexpr int kZ = kFlags;    // [cons][hi, lo][R16][64 lanes][16 B]
+  static constexpr int kFlags = kPcZOff;   // int full[8], free[8], abort
+  static constexpr int kZ = kPcZOff;       // [cons][hi, lo][R16][64 lanes][16 B]
   static constexpr int kZBytes = kPcCons * 2 * R16 * 1024;
   static constexpr int kLog = kZ + kZBytes;                           // [cons][CAP][64] (value, position)
   static constexpr int kBias = kLog + kPcCons * CAP * kWave * 8;      // [NT][2][16] f32
@@ -103,21 +104,47 @@ __device__ __forceinline__ bool pc_wait(flag_ptr f, int need, flag_ptr abort_wor
 }
 
 // ------------------------------------------------------------------ producer
+// What a producer needs: the token rows, the packed down-projection and the
+// block schedule (local block i of workgroup g is global block g + i*G).
+struct ProdArgs {
+  const void* X;
+  long long N;
+  int h;
+  const void* R1q;   // [KSP][R16][64][8] bf16: A operand (R1^T block) of each K-step
+  int KSP;           // 32-column K-steps, padded to a multiple of D (zero R1 rows)
+  int G;             // workgroups
+};
+
+// Hand-off of the producer/consumer kernel: block i goes to consumer i % 8,
+// whose private slot must have been read (freed) first.
+template <int R16>
+struct PcHandOff {
+  char* lds;
+  int limit;
+  __device__ __forceinline__ char* acquire(int i) const {
+    flag_ptr freed = pc_flags(lds) + kPcCons;
+    if (!pc_wait(freed + i % kPcCons, i / kPcCons, pc_flags(lds) + 2 * kPcCons, limit)) return nullptr;
+    return lds + kPcZOff + (i % kPcCons) * 2 * R16 * 1024;
+  }
+  __device__ __forceinline__ void publish(int i) const {
+    lds_drain();
+    pc_flags(lds)[i % kPcCons] = i / kPcCons + 1;
+  }
+};
+
 // TAIL: h is not a multiple of 32, or the K-steps are padded to a whole ring;
 // then the columns past h are replaced by out-of-range offsets (zeros).
 // Otherwise every K-step lies inside the row and its column offset is a
 // scalar, so the X loads need no per-lane arithmetic at all.
-template <int KMAX, int R16, int D, bool TAIL>
-__device__ __forceinline__ void pc_produce(const PcArgs& pa, char* lds, int p, int lane, int nbw) {
-  typedef PcLds<KMAX, R16> L;
-  const LowRankArgs& a = pa.base;
+//
+// Producer p streams local blocks i = p, p+4, ... and hands each block's z to
+// HO as bf16 hi + lo parts in the B-operand layout of the 32x32x16 MFMA.
+template <int R16, int D, bool TAIL, class HO>
+__device__ __forceinline__ void produce_z(const ProdArgs& pa, const HO& ho, int p, int lane, int nbw) {
   const int nj = (nbw - p + kPcProd - 1) / kPcProd;   // blocks of this producer
   if (nj <= 0) return;
-  flag_ptr full = pc_flags(lds);
-  flag_ptr freed = full + kPcCons;
-  flag_ptr abort_word = full + 2 * kPcCons;
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int rowbytes = a.h * 2;
+  const int rowbytes = pa.h * 2;
   const int vrow0 = l16 * rowbytes, vrow1 = (16 + l16) * rowbytes;
   const rsrc_t r1d = make_rsrc(pa.R1q, pa.KSP * R16 * 1024);
   const int NBAT = pa.KSP / D;
@@ -125,12 +152,12 @@ __device__ __forceinline__ void pc_produce(const PcArgs& pa, char* lds, int p, i
   // rows of block jj (fewer at the tail of X; none past the last block)
   auto xbase = [&](int jj) -> const char* {
     const long long b = (long long)blockIdx.x + (long long)(p + kPcProd * jj) * pa.G;
-    return (const char*)a.X + (size_t)b * kTile * rowbytes;
+    return (const char*)pa.X + (size_t)b * kTile * rowbytes;
   };
   auto xbytes = [&](int jj) -> int {
     if (jj >= nj) return 0;
     const long long b = (long long)blockIdx.x + (long long)(p + kPcProd * jj) * pa.G;
-    const long long rows = a.N - b * kTile;
+    const long long rows = pa.N - b * kTile;
     return (int)((rows < kTile ? rows : kTile) * rowbytes);
   };
 
@@ -189,11 +216,10 @@ __device__ __forceinline__ void pc_produce(const PcArgs& pa, char* lds, int p, i
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // acc[g][rb][v] = z[token 16g + l16][rank 16rb + 4q4 + v]: hand it to the consumer
+    // acc[g][rb][v] = z[token 16g + l16][rank 16rb + 4q4 + v]: hand it over
     const int i = p + kPcProd * jj;
-    const int cc = i % kPcCons, jc = i / kPcCons;
-    if (!pc_wait(freed + cc, jc, abort_word, pa.spin_limit)) return;
-    char* slot = lds + L::kZ + cc * 2 * R16 * 1024;
+    char* slot = ho.acquire(i);
+    if (!slot) return;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       // consumer lane 16g + l16 + 32(q4&1), elements 4(q4>>1) .. +3 of K-step rb
@@ -213,8 +239,7 @@ __device__ __forceinline__ void pc_produce(const PcArgs& pa, char* lds, int p, i
         *(uint2*)(slot + (R16 + rb) * 1024 + off) = make_uint2(lv[0], lv[1]);
       }
     }
-    lds_drain();
-    full[cc] = jc + 1;
+    ho.publish(i);
     cbase = nbase;
     cbytes = nbytes;
     nbase = xbase(jj + 2);
@@ -332,7 +357,8 @@ __global__ __launch_bounds__(64 * kPcWaves) void pc_kernel(PcArgs pa) {
   __syncthreads();
   const int nbw = (pa.NB - (int)blockIdx.x + pa.G - 1) / pa.G;   // blocks of this workgroup
   if (wave < kPcProd)
-    pc_produce<KMAX, R16, D, TAIL>(pa, pc_lds, wave, lane, nbw);
+    produce_z<R16, D, TAIL>(ProdArgs{pa.base.X, pa.base.N, pa.base.h, pa.R1q, pa.KSP, pa.G},
+                            PcHandOff<R16>{pc_lds, pa.spin_limit}, wave, lane, nbw);
   else
     pc_consume<KMAX, FULL, R16>(pa, pc_lds, wave - kPcProd, lane, nbw);
 }

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -109,6 +110,28 @@ more_status validate(int fullrank, more_dtype dt, const void* X, int64_t N, int6
 }
 
 // ---------------------------------------------------------------- dispatch
+// Kernel paths of the low-rank router, in the order they are tried (measured
+// fastest first on the workloads they share).  Each call takes the first one
+// whose shape envelope fits.  MORE_ROUTE_PATHS (environment, read at
+// every call) can restrict the candidates to a comma-separated subset of
+// "pc,slice,lock,stream,simple" -- a testing aid so that every path can be
+// checked on the shapes a faster one would take; "simple" always fits.
+enum { kPathPc = 1, kPathSlice = 2, kPathLock = 4, kPathStream = 8 };
+bool path_allowed(int path) {
+  const char* env = getenv("MORE_ROUTE_PATHS");
+  if (!env || !*env) return true;
+  const char* name = path == kPathSlice ? "slice" : path == kPathPc ? "pc" : path == kPathLock ? "lock" : "stream";
+  const size_t len = strlen(name);
+  for (const char* p = env; *p;) {
+    const char* e = strchr(p, ',');
+    const size_t n = e ? (size_t)(e - p) : strlen(p);
+    if (n == len && strncmp(p, name, len) == 0) return true;
+    if (!e) break;
+    p = e + 1;
+  }
+  return false;
+}
+
 lowrank_fn pick_lowrank(more_dtype dt, bool full, int kmax, int r16) {
   if (dt == MORE_DT_BF16) return full ? pick_lowrank_bf16_full(kmax, r16) : pick_lowrank_bf16_topk(kmax, r16);
   return pick_lowrank_f32(full, kmax, r16);
@@ -236,7 +259,7 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   a.out_lse = full ? lse : nullptr;
   const size_t shmem = (size_t)waves * log_bytes(kmax);
   const size_t pc_lds = (dt == MORE_DT_BF16 && L.ksq > 0) ? pc_lds_bytes(kmax, L.r16, L.Mpad) : 0;
-  if (pc_lds > 0 && (long long)pc_lds <= kLdsBytes) {
+  if (pc_lds > 0 && (long long)pc_lds <= kLdsBytes && path_allowed(kPathPc)) {
     // Producer/consumer kernel: one 12-wave workgroup per CU, persistent.
     int ksp = 0;
     bool tail = false;
@@ -260,7 +283,33 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
     hipLaunchKernelGGL(fn, dim3((unsigned)pa.G), dim3(64 * kPcWaves), pc_lds, (hipStream_t)stream, pa);
     return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
   }
-  if (dt == MORE_DT_BF16 && lock_supported(kmax, L.r16, L.Mpad)) {
+  const size_t sl_lds = (dt == MORE_DT_BF16 && L.ksq > 0 && slice_shape_ok(kmax, L.r16, L.Mpad))
+                            ? slice_lds_bytes(full, L.r16) : 0;
+  if (sl_lds > 0 && (long long)sl_lds <= kLdsBytes && path_allowed(kPathSlice)) {
+    // Expert-slice kernel: one 12-wave workgroup per CU, persistent.
+    int ksp = 0;
+    bool tail = false;
+    pc_ksteps(h, L.r16, &ksp, &tail);
+    slice_fn fn = pick_slice(full, L.r16, tail);
+    int dev = 0, cus = 0;
+    if (!fn || hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sl_lds) !=
+            hipSuccess)
+      return MORE_ERR_HIP;
+    SlArgs sa;
+    sa.base = a;
+    const int64_t nb = (N + kTile - 1) / kTile;
+    if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
+    sa.NB = (int)nb;
+    sa.G = (int)std::max<int64_t>(1, std::min<int64_t>(cus, nb));
+    sa.KSP = L.ksq;
+    sa.R1q = ws + L.off_r1q;
+    sa.spin_limit = 1 << 22;
+    hipLaunchKernelGGL(fn, dim3((unsigned)sa.G), dim3(64 * kSlWaves), sl_lds, (hipStream_t)stream, sa);
+    return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+  }
+  if (dt == MORE_DT_BF16 && lock_supported(kmax, L.r16, L.Mpad) && path_allowed(kPathLock)) {
     // Workgroup-lockstep kernel, one 8-wave workgroup per CU, persistent.
     size_t lds = 0;
     lock_fn fn = pick_lock(full, kmax, L.r16, &lds);
@@ -283,7 +332,7 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
     hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(64 * kLockWaves), lds, (hipStream_t)stream, la);
     return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
   }
-  if (dt == MORE_DT_BF16 && stream_supported(L.r16)) {
+  if (dt == MORE_DT_BF16 && stream_supported(L.r16) && path_allowed(kPathStream)) {
     // Persistent grid: as many waves as fit on the device at once, each owning
     // an equal number of 32-token blocks.
     stream_fn fn = pick_stream(full, kmax, L.r16);
