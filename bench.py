@@ -30,6 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+# the fused router kernel the headline workload dispatches to (rocprofv3 name)
+KERNEL_NAME = "more::pc_kernel<8, false, 2, 8, false>"
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published (no sparsity)
 CONTEXT = {
     "source": "MoRE: Scaling mixture of experts with hardware-aware low-rank routing (B200, bf16)",
@@ -56,7 +58,85 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fullrank", action="store_true")
     ap.add_argument("--fullrank-steps", type=int, default=3)
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, "
+                         "both with --calib-copy) into profiles/traffic_<workload>.json and exit")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain device copy of 256 MiB three times (byte-counter calibration "
+                         "for rocprofv3 --pmc runs)")
     return ap.parse_args()
+
+
+def source_hash():
+    """Hash of the HIP sources the library is built from: traffic counters taken
+    on another version of the kernels are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_router_top_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter(run_dir, counter):
+    """Per-dispatch mean of `counter` (KiB) for the router kernel and the copy
+    kernel in a rocprofv3 --pmc CSV (rows are per dimension instance; summed
+    per dispatch)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                kind = "router" if KERNEL_NAME.split("<")[0] in name else (
+                    "copy" if "copyBuffer" in name else None)
+                if kind:
+                    key = (kind, row["Dispatch_Id"])
+                    per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for kind in ("router", "copy"):
+        vals = [v for (k, _), v in per.items() if k == kind]
+        if kind == "copy" and vals:
+            # the calibration copies (256 MiB) are the large ones; the runtime
+            # also copies the small inputs with the same kernel
+            vals = [v for v in vals if v >= 0.5 * max(vals)]
+        if not vals:
+            raise SystemExit(f"no {kind} dispatches with {counter} in {run_dir}")
+        out[kind] = (sum(vals) / len(vals), len(vals))
+    return out
+
+
+def write_traffic(args):
+    from rank_router_top_amd import configs as CF
+    cfg = CF.ALL[args.workload]
+    copy_bytes = 256 << 20
+    fetch = read_counter(args.traffic_from[0], "FETCH_SIZE")
+    write = read_counter(args.traffic_from[1], "WRITE_SIZE")
+    f_fac = copy_bytes / (fetch["copy"][0] * 1024.0)
+    w_fac = copy_bytes / (write["copy"][0] * 1024.0)
+    fb = fetch["router"][0] * 1024.0 * f_fac
+    wb = write["router"][0] * 1024.0 * w_fac
+    alg = algorithmic_bytes(cfg, cfg.k, False)
+    res = {"workload": cfg.name, "kernel": KERNEL_NAME, "source_hash": source_hash(),
+           "bytes_per_launch": fb + wb, "fetch_bytes": fb, "write_bytes": wb,
+           "algorithmic_bytes": alg, "traffic_over_algorithmic": (fb + wb) / alg,
+           "fetch_factor": f_fac, "write_factor": w_fac,
+           "router_dispatches": [fetch["router"][1], write["router"][1]],
+           "copy_bytes": copy_bytes}
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res))
+    return 0
 
 
 def algorithmic_bytes(cfg, k, with_lse):
@@ -89,6 +169,8 @@ def time_events(torch, fn, steps, stream):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        return write_traffic(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this router benchmark runs on exactly one GPU; "
                                    "multi-GPU runs are not supported (token sharding would need no "
@@ -155,14 +237,16 @@ def main():
     alg_bytes = algorithmic_bytes(cfg, cfg.k, False)
     achieved = alg_bytes / (k_mean * 1e-3) / 1e9
     rt = roofline_time_s(cfg)
+    # HBM bytes per launch from the committed rocprofv3 counter runs (FETCH_SIZE,
+    # WRITE_SIZE, scaled by the same counters on a copy of known size); only
+    # when they were taken on the current kernel sources
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
     if os.path.exists(tpath):
-        try:
-            tr = json.load(open(tpath))
+        with open(tpath) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == source_hash():
             traffic = tr.get("bytes_per_launch")
-        except Exception:
-            traffic = None
 
     result = {
         "metric": "routed tokens/sec & % roofline, N=262144 h=2048 M=4096 r=32 k=8, 1 GPU",
@@ -184,7 +268,7 @@ def main():
         "roofline_time_us": rt * 1e6,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "lowrank_kernel", "kernel_ms": k_mean, "kernel_ms_median": k_med,
+                     "kernel": KERNEL_NAME, "kernel_ms": k_mean, "kernel_ms_median": k_med,
                      "kernel_ms_p10": k_p10, "kernel_ms_p90": k_p90,
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "mfma_tflops": cfg.flops() / (k_mean * 1e-3) / 1e12,
@@ -230,6 +314,14 @@ def main():
                                   "sample": f"first {n} of the {cfg.N} tokens, same weights, fp64, "
                                             f"{dt_cpu:.1f} s wall"}
         log(f"cpu oracle {n / dt_cpu:.0f} tokens/s on {threads} threads")
+
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = src.numel()
 
     print(json.dumps(result), flush=True)
     return 0
