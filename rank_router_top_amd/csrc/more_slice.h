@@ -89,7 +89,8 @@ struct SlLds {
   static constexpr int kLog = kPerm + kSlNT * 64;               // [32][kSlLogStride] (logit, position / expert)
   static constexpr int kExch = kLog + 32 * kSlLogStride * 8;    // [32][16 lane halves] 2 x f32
   static constexpr int kMZ = kExch + 32 * 16 * 8;               // FULL: [2][32][16] (m, Z)
-  static constexpr int bytes = kMZ + (FULL ? 2 * 32 * 16 * 8 : 0);
+  static constexpr int kStage = kMZ + (FULL ? 2 * 32 * 16 * 8 : 0);   // [32][kSlK] (expert, gate)
+  static constexpr int bytes = kStage + 32 * kSlK * 8;
 };
 
 // Producer side of the ring: block i goes to slot i % NZ once every consumer
@@ -157,8 +158,8 @@ __device__ __forceinline__ bool beats(float a, int ia, float b, int ib) {
 // the masked columns store the result.  App. F.1 Algorithm 1 in its plain
 // form (one running top-k per token over all experts).
 template <bool FULL, bool BIAS, int R16>
-__device__ __forceinline__ void sl_slow(const LowRankArgs& a, const char* zs, int lane, uint32_t tok_mask,
-                                     long long n0) {
+__device__ __forceinline__ void sl_slow(const LowRankArgs& a, const char* zs, int2* stage, int lane,
+                                       uint32_t tok_mask, long long n0) {
   const int hf = lane >> 5, tl = lane & 31;
   bf16x8 zh[R16], zl[R16];
 #pragma unroll
@@ -234,8 +235,7 @@ __device__ __forceinline__ void sl_slow(const LowRankArgs& a, const char* zs, in
 #pragma unroll
   for (int j = 0; j < kSlK; ++j) {
     if (j < k) {
-      a.out_idx[o + j] = IX[j];
-      a.out_gate[o + j] = w[j] * inv;
+      stage[tl * kSlK + j] = make_int2(IX[j], __float_as_int(w[j] * inv));
       if (a.out_logit) a.out_logit[o + j] = V[j];
     }
   }
@@ -323,6 +323,28 @@ __device__ __forceinline__ void sl_consume(const SlArgs& sa, char* lds, int c, i
   }
   const float cmax = __builtin_sqrtf(cmax2) * (1.f + 0x1p-16f);   // covers the fp32 sums and the root
 
+  // Results leave through a staging area: the finish of block j puts this
+  // wave's (expert, gate) pairs there, and the same wave stores them during
+  // block j + 1, right after the first tile of pass 2.  The consumer issues no
+  // other global memory operation in the loop, so those stores can take as
+  // long as writes take under the X stream without any wait of the wave on
+  // them (a vector-memory wait would also wait for every earlier store).
+  int2* stage = (int2*)(lds + L::kStage);
+  auto copy_out = [&](int jb) {
+    // tokens 4c .. 4c+3 of block jb: lane -> token 4c + lane/16, ranks 2(lane%16) .. +1
+    const int t = 4 * c + (lane >> 4), r = 2 * (lane & 15);
+    const long long n = ((long long)blockIdx.x + (long long)jb * sa.G) * kTile + t;
+    if (r < k && n < a.N) {
+      const int4 v = *(const int4*)(stage + t * kSlK + r);   // pairs r, r + 1
+      const size_t o = (size_t)n * k + r;
+      a.out_idx[o] = v.x;
+      a.out_gate[o] = __int_as_float(v.y);
+      if (r + 1 < k) {
+        a.out_idx[o + 1] = v.z;
+        a.out_gate[o + 1] = __int_as_float(v.w);
+      }
+    }
+  };
   for (int jj = 0; jj < nbw; ++jj) {
     const int slot = jj % NZ;
     if (!pc_wait(fl + kSlFull + slot, jj + 1, abort_word, limit)) return;
@@ -466,6 +488,10 @@ __device__ __forceinline__ void sl_consume(const SlArgs& sa, char* lds, int c, i
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // one tile at a time (register pressure)
+      if (i == 0 && jj > 0) {
+        copy_out(jj - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (!sl_bar(fl + kSlBar2, kSlCons * (jj + 1), abort_word, limit, lane)) return;
 
@@ -528,13 +554,11 @@ __device__ __forceinline__ void sl_consume(const SlArgs& sa, char* lds, int c, i
       if (n < a.N) {
         const size_t o = (size_t)n * k;
         if (s0) {
-          a.out_idx[o + r0] = i0;
-          a.out_gate[o + r0] = g0;
+          stage[nloc * kSlK + r0] = make_int2(i0, __float_as_int(g0));
           if (a.out_logit) a.out_logit[o + r0] = e0.x;
         }
         if (s1) {
-          a.out_idx[o + r1] = i1;
-          a.out_gate[o + r1] = g1;
+          stage[nloc * kSlK + r1] = make_int2(i1, __float_as_int(g1));
           if (a.out_logit) a.out_logit[o + r1] = e1.x;
         }
         if (FULL && j16 == 0 && !ovf && a.out_lse) a.out_lse[n] = lse;
@@ -547,10 +571,11 @@ __device__ __forceinline__ void sl_consume(const SlArgs& sa, char* lds, int c, i
         for (int t = 0; t < 4; ++t)
           if ((om >> (16 * t)) & 1) tok_mask |= 1u << (4 * c + t);
         const long long n0 = ((long long)blockIdx.x + (long long)jj * sa.G) * kTile;
-        sl_slow<FULL, BIAS, R16>(a, zs, lane, tok_mask, n0);
+        sl_slow<FULL, BIAS, R16>(a, zs, stage, lane, tok_mask, n0);
       }
     }
   }
+  if (nbw > 0) copy_out(nbw - 1);
 }
 
 template <bool FULL, bool BIAS, int R16, int TV, int NZ, int D, bool TAIL>
