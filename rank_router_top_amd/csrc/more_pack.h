@@ -15,6 +15,8 @@
 
 namespace more {
 
+constexpr int kPackLdsM = 16384;   // largest M whose bias the sweep-order blocks stage in LDS
+
 // Position p of the sweep holds expert perm[p] (perm[p] = -1 on the padding
 // positions M..M_pad-1).  Row i of tile t is position 32t + i.  For a lane of
 // half hf, accumulator register v holds row 8*(v>>2) + 4*hf + (v&3).
@@ -71,10 +73,27 @@ __global__ __launch_bounds__(1024) void pack_kernel(PackArgs a) {
   if ((int)blockIdx.x < a.rank_blocks) {
     // ---- sweep order: rank of expert j by (bias desc, index asc); padding last
     __shared__ int part[16][64];
+    __shared__ float4 bsh[kPackLdsM / 4];   // the bias, when it fits (read by broadcast)
     const int jl = tid & 63, slice = tid >> 6;   // 64 experts x 16 slices
     const int j = blockIdx.x * 64 + jl;
     int cnt = 0;
-    if (a.bias && j < a.M) {
+    if (a.bias && a.M <= kPackLdsM && (a.M & 3) == 0) {
+      for (int i = tid; i < a.M / 4; i += 1024) bsh[i] = ((const float4*)a.bias)[i];
+      __syncthreads();
+      if (j < a.M) {
+        const float bj = a.bias[j];
+        // slice s compares against experts 4q .. 4q+3 for q = s, s + 16, ... (all
+        // 64 lanes of a wave read the same float4)
+        for (int q = slice; q < a.M / 4; q += 16) {
+          const float4 b4 = bsh[q];
+          const int i = 4 * q;
+          cnt += (b4.x > bj) || (b4.x == bj && i < j);
+          cnt += (b4.y > bj) || (b4.y == bj && i + 1 < j);
+          cnt += (b4.z > bj) || (b4.z == bj && i + 2 < j);
+          cnt += (b4.w > bj) || (b4.w == bj && i + 3 < j);
+        }
+      }
+    } else if (a.bias && j < a.M) {
       const float bj = a.bias[j];
       const int per = (a.M + 15) / 16;
       const int i0 = slice * per, i1 = min(a.M, i0 + per);
