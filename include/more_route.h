@@ -50,9 +50,12 @@
  *   with lse = log sum over all M experts of exp(l) (not renormalised).
  *   Workspace.  Device scratch owned by the caller, at least
  *   more_route_workspace_bytes(...) bytes for the same arguments, 256-byte
- *   aligned.  It carries the per-call packed weights and, for small token
- *   counts, partial results.  Its contents need no initialisation and are
- *   garbage afterwards.  Two calls in flight must not share a workspace.
+ *   aligned.  It carries the per-call packed weights, then (low rank, bf16,
+ *   r <= 64) token scratch sized by N: the rank-r intermediate z of every
+ *   32-token block (4 bytes per token and rank) for the two-kernel path.  A
+ *   workspace without room for that scratch is still valid; the routing call
+ *   then takes a one-kernel path.  Its contents need no initialisation and
+ *   are garbage afterwards.  Two calls in flight must not share a workspace.
  */
 #ifndef MORE_ROUTE_H
 #define MORE_ROUTE_H
@@ -122,7 +125,9 @@ more_status more_route_lowrank(more_dtype dt, const void* X, int64_t N, int64_t 
  * agree on dt, h, r and M (and on whether a bias was given); the library
  * cannot check this because the packed data lives on the device.
  * more_route_lowrank(...) is exactly more_lowrank_pack followed by
- * more_lowrank_route_packed on the same stream.
+ * more_lowrank_route_packed on the same stream.  more_lowrank_route_packed
+ * only reads the packed part of the workspace; it overwrites the token
+ * scratch behind it (used when workspace_bytes covers N tokens).
  */
 more_status more_lowrank_pack(more_dtype dt, const void* R1, int64_t h, int64_t r, const void* R2,
                               int64_t M, const float* bias, void* workspace, size_t workspace_bytes,
@@ -130,7 +135,7 @@ more_status more_lowrank_pack(more_dtype dt, const void* R1, int64_t h, int64_t 
 more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int64_t r,
                                       int64_t M, int32_t k, more_gate gate, int32_t* topk_idx,
                                       float* topk_gate, float* topk_logit, float* lse,
-                                      const void* workspace, size_t workspace_bytes, void* stream);
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Fused standard (full-rank) router + top-k + gates: the same selection and

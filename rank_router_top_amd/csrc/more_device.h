@@ -28,6 +28,25 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+// Explicit LDS pointers: accesses through them are ds_* instructions (a
+// generic pointer may become FLAT, which also waits on the vector-memory counter).
+typedef __attribute__((address_space(3))) int lds_i32;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) const uint16_t lds_cu16;
+typedef __attribute__((address_space(3))) floatx4 lds_f4;
+typedef __attribute__((address_space(3))) const char lds_cchar;
+typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
+typedef __attribute__((address_space(3))) const bf16x8 lds_cbf16x8;
+// Workgroup-wide OR of v through one LDS word (no static LDS; two barriers).
+__device__ __forceinline__ bool block_any(bool v, lds_i32* word) {
+  if (threadIdx.x == 0) *word = 0;
+  __syncthreads();
+  if (v) *word = 1;
+  __syncthreads();
+  return *word != 0;
+}
+// 16 bytes of LDS at byte offset off from p (a ds_read_b128)
+__device__ __forceinline__ u32x4 lds_ld128(lds_cchar* p, int off) { return *(lds_cu32x4*)(p + off); }
 
 constexpr int kWave = 64;
 constexpr int kTile = 32;                // experts per tile == tokens per wave
@@ -65,9 +84,10 @@ struct LogRef {
 // only the k ties of lowest expert index (the tie rule): entries of higher rank
 // among the ties can never be selected.  Called with the whole wave active.
 // Kept out of line: it is rare, and its perm[] lookups (global loads) would
-// otherwise force conservative memory waits into the sweep loops.
-__device__ __noinline__ int compact_log(float2* base, int lane, int cnt, float thr,
-                                        const int* __restrict__ perm, int k, int cap) {
+// otherwise force conservative memory waits into the sweep loops.  PT: any
+// pointer whose [] yields the expert index (global int, or an LDS copy).
+template <class PT>
+__device__ __noinline__ int compact_log(float2* base, int lane, int cnt, float thr, PT perm, int k, int cap) {
   int w = 0;
   for (int c = 0; c < cnt; ++c) {
     const float2 e = base[c * kWave + lane];

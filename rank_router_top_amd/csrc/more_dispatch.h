@@ -7,6 +7,7 @@
 #include "more_lock.h"
 #include "more_pc.h"
 #include "more_slice.h"
+#include "more_split.h"
 
 namespace more {
 
@@ -53,6 +54,29 @@ constexpr bool pc_shape_ok(int kmax, int r16, long long mpad) {
 // Dynamic LDS of the instance for (kmax, r16, mpad); 0 if no instance exists.
 size_t pc_lds_bytes(int kmax, int r16, long long mpad);
 pc_fn pick_pc(bool full, int kmax, int r16, bool tail);
+
+// Two-kernel form (projection + routing): bf16, k <= 8, r <= 64, M <= 65535.
+typedef void (*proj_fn)(ProjArgs);
+typedef void (*route_fn)(RouteArgs);
+constexpr int kProjWaves = 4;    // projection: one streaming wave per SIMD (+1 writer), one workgroup per CU
+constexpr int kRouteWaves = 8;   // routing: eight waves, one workgroup per CU
+// Projection ring depth (K-steps in flight per wave).
+constexpr int proj_depth(int r16) { return 8; }
+// K-steps the projection processes (a multiple of its ring depth) and whether
+// the X loads need per-lane column checks.
+inline void proj_ksteps(long long h, int r16, int* ksp, bool* tail) {
+  const long long ks = (h + 31) / 32;
+  const int D = proj_depth(r16);
+  *tail = (h % 32 != 0) || (ks % D != 0);
+  *ksp = (int)((ks + D - 1) / D * D);
+}
+constexpr bool split_shape_ok(int kmax, int r16, long long mpad) {
+  return kmax <= 8 && r16 <= 4 && mpad <= 65535;
+}
+proj_fn pick_proj(int r16, bool tail);
+route_fn pick_route(bool full, int kmax, int r16);
+size_t route_lds_bytes(int kmax, long long mpad);
+size_t proj_lds_bytes(int r16, int ksp);
 
 // Expert-slice kernel: bf16, r in {16, 32}, M = 4096 (128 tiles), k <= 8.
 // LDS bytes (0: no instance) and instance.

@@ -18,10 +18,16 @@
 //     16-byte load of 16 rows x 64 bytes delivers (no LDS transpose); at the
 //     end of a 32-token block they split z into bf16 hi + lo parts and write
 //     them into the LDS slot of the consumer that owns the block;
-//   8 consumer waves: read z from their slot (then free it), and sweep all
+//   8 consumer waves: read z from their slot (then free it), and compute
 //     expert tiles with v_mfma_f32_32x32x16_bf16: logits^T = R2^T z + bias
-//     (bias enters as the fp32 accumulator input, staged once in LDS), with
-//     the two-pass exact top-k of more_twopass.h.
+//     (bias enters as the fp32 accumulator input, staged once in LDS): a
+//     short seed pass over the first `pre` tiles of the bias-descending order
+//     (pass 1 of more_twopass.h: a lower bound of each token's k-th logit),
+//     then one sweep over all tiles that raises the bound and logs what
+//     reaches it (tp_sweep_tile).  With a bias, the high-bias tiles at the
+//     front hold most of the winners, so the seeded bound is close to the
+//     final k-th logit and the log stays short; each expert tile costs ~1.2
+//     sweeps instead of 2.
 //
 // Hand-off: per consumer, two LDS counters (blocks produced / blocks read).
 // Each wait is a bounded spin: if a counter does not move within spin_limit
@@ -46,7 +52,12 @@ constexpr int kPcCons = 8;                     // consumer waves per workgroup
 constexpr int kPcWaves = kPcProd + kPcCons;
 constexpr int kBufWord3 = 0x00020000;          // raw buffer, 32-bit data format
 constexpr int kOob = 0x40000000;               // offset past any descriptor range: loads 0
-constexpr int kPcZOff = 128;                   // LDS: hand-off counters, then the z slots
+constexpr int kPcZOff = 256;                   // LDS: hand-off counters, then the z slots
+// Seed-pass length in expert tiles (multiple of 4).  With the experts swept in
+// bias-descending order, 24 tiles (768 experts) already bound a token's k-th
+// logit closely: a simulation of the N(0,1) + N(0,0.5)-bias logits at M = 4096,
+// k = 8 logs ~12 entries per token in the sweep (max 24 over 4096 tokens).
+constexpr int kPcSeedTiles = 24;
 
 struct PcArgs {
   LowRankArgs base;    // X, N, h, NT (multiple of 4), k, R2p, biasp, perm, outputs
@@ -55,18 +66,29 @@ struct PcArgs {
   int G;               // workgroups
   int KSP;             // 32-column K-steps, padded to a multiple of D (zero R1 rows)
   int spin_limit;      // polls before a wait gives up
+  int pre;             // seed-pass tiles: a multiple of 4 in [4, NT]
 };
 
-// LDS map (bytes): flags | z slots | logs | bias
+// Hand-off counters (ints at the start of LDS)
+constexpr int kPcFull = 0;       // [cons] z blocks published
+constexpr int kPcFreed = 8;      // [cons] z blocks read
+constexpr int kPcAbort = 16;
+constexpr int kPcStaged = 17;    // [cons] result blocks written to the consumer's staging area
+constexpr int kPcDrained = 25;   // [cons] result blocks read back out by the producer
+constexpr int kPcAnyBias = 63;   // set-up only: does any expert have a nonzero bias
+
+// LDS map (bytes): flags | z slots | logs | result staging | bias | perm (u16)
 template <int KMAX, int R16>
 struct PcLds {
-  static constexpr int CAP = Cap<KMAX>::value;
-  static constexpr int kFlags = kPcZOff;   // int full[8], free[8], abort
+  static constexpr int CAP = KMAX + 8;     // log entries per lane (compacted when nearly full)
   static constexpr int kZ = kPcZOff;       // [cons][hi, lo][R16][64 lanes][16 B]
   static constexpr int kZBytes = kPcCons * 2 * R16 * 1024;
-  static constexpr int kLog = kZ + kZBytes;                           // [cons][CAP][64] (value, position)
-  static constexpr int kBias = kLog + kPcCons * CAP * kWave * 8;      // [NT][2][16] f32
-  static constexpr size_t bytes(long long mpad) { return (size_t)kBias + (size_t)mpad * 4; }
+  static constexpr int kLog = kZ + kZBytes;                            // [cons][CAP][64] (value, position)
+  static constexpr int kStage = kLog + kPcCons * CAP * kWave * 8;      // [cons] TpStage<KMAX>
+  static constexpr int kStageBytes = TpStage<KMAX>::kWords * 4;
+  static constexpr int kBias = kStage + kPcCons * kStageBytes;         // [NT][2][16] f32
+  static constexpr size_t perm_off(long long mpad) { return (size_t)kBias + (size_t)mpad * 4; }
+  static constexpr size_t bytes(long long mpad) { return perm_off(mpad) + (size_t)mpad * 2; }
 };
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
@@ -84,7 +106,6 @@ __device__ __forceinline__ void lds_drain() { asm volatile("s_waitcnt lgkmcnt(0)
 // also counts against the vector-memory counter, and waiting for it would
 // drain every load in flight (the X ring of a producer, the operand ring of a
 // consumer).
-typedef __attribute__((address_space(3))) int lds_i32;
 typedef volatile lds_i32* flag_ptr;
 __device__ __forceinline__ flag_ptr pc_flags(char* lds) { return (flag_ptr)(lds_i32*)lds; }
 
@@ -117,18 +138,75 @@ struct ProdArgs {
 
 // Hand-off of the producer/consumer kernel: block i goes to consumer i % 8,
 // whose private slot must have been read (freed) first.
-template <int R16>
+//
+// The results travel back the same way: a consumer writes each finished
+// block into its LDS staging area, and the producer that feeds it (consumer c
+// is always fed by producer c % 4) stores them to HBM.  A consumer's global
+// stores would otherwise sit in its own vector-memory counter, which counts
+// loads and stores in issue order: every later wait for a weight tile would
+// also wait for those stores, and under the saturated X stream a store takes
+// microseconds to be acknowledged.  In the producer the few stores per block
+// are hidden behind the X loads that are in flight anyway.
+template <int KMAX, int R16>
 struct PcHandOff {
   char* lds;
   int limit;
+  int* out_idx;
+  float* out_gate;
+  float* out_logit;   // may be null
+  float* out_lse;     // null unless the full-softmax normaliser is wanted
+  long long N;
+  int k, G, nbw;
+
+  __device__ __forceinline__ flag_ptr flags() const { return pc_flags(lds); }
   __device__ __forceinline__ char* acquire(int i) const {
-    flag_ptr freed = pc_flags(lds) + kPcCons;
-    if (!pc_wait(freed + i % kPcCons, i / kPcCons, pc_flags(lds) + 2 * kPcCons, limit)) return nullptr;
+    if (!pc_wait(flags() + kPcFreed + i % kPcCons, i / kPcCons, flags() + kPcAbort, limit)) return nullptr;
     return lds + kPcZOff + (i % kPcCons) * 2 * R16 * 1024;
   }
   __device__ __forceinline__ void publish(int i) const {
     lds_drain();
-    pc_flags(lds)[i % kPcCons] = i / kPcCons + 1;
+    flags()[kPcFull + i % kPcCons] = i / kPcCons + 1;
+  }
+  // Store result block r of consumer c (local block c + 8r).
+  __device__ __forceinline__ bool drain(int c, int r, int lane) const {
+    typedef TpStage<KMAX> S;
+    if (!pc_wait(flags() + kPcStaged + c, r + 1, flags() + kPcAbort, limit)) return false;
+    const char* stg = lds + PcLds<KMAX, R16>::kStage + c * PcLds<KMAX, R16>::kStageBytes;
+    const u32x4 vi = *(const u32x4*)(stg + S::kIdx * 4 + lane * 16);
+    const u32x4 vg = *(const u32x4*)(stg + S::kGate * 4 + lane * 16);
+    u32x4 vl = {}, vz = {};
+    if (out_logit) vl = *(const u32x4*)(stg + S::kLogit * 4 + lane * 16);
+    if (out_lse) vz = *(const u32x4*)(stg + S::kLse * 4 + lane * 16);
+    lds_drain();
+    flags()[kPcDrained + c] = r + 1;
+    const long long b = (long long)blockIdx.x + (long long)(c + kPcCons * r) * G;
+    const long long n0 = b * kTile;
+    const long long rows = N - n0 < kTile ? N - n0 : kTile;
+    // one 16-byte store per lane covers a whole array (32 k <= 256 words);
+    // the descriptor range drops the lanes past the block's valid rows
+    const int bk = (int)rows * k * 4;
+    const u32x4 v[2] = {vi, vg};
+    void* dst[2] = {out_idx + n0 * k, out_gate + n0 * k};
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_buffer_store_b128(v[q], make_rsrc(dst[q], bk), lane * 16, 0, 0);
+    if (out_logit) __builtin_amdgcn_raw_buffer_store_b128(vl, make_rsrc(out_logit + n0 * k, bk), lane * 16, 0, 0);
+    if (out_lse) __builtin_amdgcn_raw_buffer_store_b128(vz, make_rsrc(out_lse + n0, (int)rows * 4), lane * 16, 0, 0);
+    return true;
+  }
+  // After block i was handed over: results of consumer i % 8 two rounds back.
+  __device__ __forceinline__ bool retire(int i, int lane) const {
+    const int r = i / kPcCons - 2;
+    return r < 0 || drain(i % kPcCons, r, lane);
+  }
+  // After the producer's last block: the remaining results of its consumers
+  // (the last two rounds of each), older rounds first.
+  __device__ __forceinline__ void finish(int p, int lane) const {
+    for (int back = 2; back >= 1; --back)
+      for (int c = p; c < kPcCons; c += kPcProd) {
+        const int r = (nbw - c + kPcCons - 1) / kPcCons - back;   // blocks of consumer c, minus back
+        if (r >= 0 && !drain(c, r, lane)) return;
+      }
   }
 };
 
@@ -138,7 +216,9 @@ struct PcHandOff {
 // scalar, so the X loads need no per-lane arithmetic at all.
 //
 // Producer p streams local blocks i = p, p+4, ... and hands each block's z to
-// HO as bf16 hi + lo parts in the B-operand layout of the 32x32x16 MFMA.
+// HO as bf16 hi + lo parts in the B-operand layout of the 32x32x16 MFMA
+// (HO: acquire(i) -> slot, publish(i), retire(i, lane) after each hand-over,
+// finish(p, lane) after the last block).
 template <int R16, int D, bool TAIL, class HO>
 __device__ __forceinline__ void produce_z(const ProdArgs& pa, const HO& ho, int p, int lane, int nbw) {
   const int nj = (nbw - p + kPcProd - 1) / kPcProd;   // blocks of this producer
@@ -240,29 +320,32 @@ __device__ __forceinline__ void produce_z(const ProdArgs& pa, const HO& ho, int 
       }
     }
     ho.publish(i);
+    if (!ho.retire(i, lane)) return;
     cbase = nbase;
     cbytes = nbytes;
     nbase = xbase(jj + 2);
     nbytes = xbytes(jj + 2);
   }
+  ho.finish(p, lane);
 }
 
 // ------------------------------------------------------------------ consumer
 template <int KMAX, bool FULL, int R16>
-__device__ __forceinline__ void pc_consume(const PcArgs& pa, char* lds, int c, int lane, int nbw) {
+__device__ __forceinline__ void pc_consume(const PcArgs& pa, char* lds, int c, int lane, int nbw, bool has_bias) {
   typedef PcLds<KMAX, R16> L;
   constexpr int CAP = L::CAP;
   const LowRankArgs& a = pa.base;
   const int nj = (nbw - c + kPcCons - 1) / kPcCons;
   if (nj <= 0) return;
-  flag_ptr full = pc_flags(lds);
-  flag_ptr freed = full + kPcCons;
-  flag_ptr abort_word = full + 2 * kPcCons;
+  flag_ptr fl = pc_flags(lds);
+  flag_ptr abort_word = fl + kPcAbort;
   const bool hi = lane >= 32;
   const int hf = hi ? 1 : 0;
   LogRef lg{(float2*)(lds + L::kLog) + c * CAP * kWave};
   const float* lb = (const float*)(lds + L::kBias);
   const char* slot = lds + L::kZ + c * 2 * R16 * 1024;
+  lds_f32* stg = (lds_f32*)(lds + L::kStage + c * L::kStageBytes);
+  lds_cu16* perm = (lds_cu16*)(lds + L::perm_off(a.NT * kTile));
   const int NT = a.NT;
   const rsrc_t r2d = make_rsrc(a.R2p, NT * R16 * 1024);
 
@@ -284,33 +367,35 @@ __device__ __forceinline__ void pc_consume(const PcArgs& pa, char* lds, int c, i
     for (int m = 0; m < R16; ++m) acc = mfma_bf16(o.w[m], zl[m], acc);
     return acc;
   };
-  auto wrap = [&](int t) { return t >= NT ? t - NT : t; };   // t < 2 NT
+  // seed-pass length: the full-softmax gate needs pass 1 over every tile, and
+  // without a bias the sweep order carries no hint (plain two passes)
+  const int P = (FULL || !has_bias) ? NT : pa.pre;
 
-  // Software pipeline over the expert tiles (NT is a multiple of 4): at step t
-  // the VALU works on tile t while the MFMAs of tile t+1 run; the weight
-  // operands of tile t+1 were requested at step t-4 (a 4-slot register ring,
-  // so three newer requests may still be in flight: the wait never reaches
-  // back to a recent L2 request) and its bias (LDS) at step t-2.  The ring
-  // wraps into the next pass's first tiles at the end of a pass.  Each block
-  // is swept twice (more_twopass.h): pass 1 finds the token threshold, pass 2
-  // logs the logits that reach it.
+  // Software pipeline over the expert tiles (pass lengths are multiples of 4):
+  // at step t the VALU works on tile t while the MFMAs of tile t+1 run; the
+  // weight operands of tile t+1 were requested at step t-4 (a 4-slot register
+  // ring, so three newer requests may still be in flight: the wait never
+  // reaches back to a recent L2 request) and its bias (LDS) at step t-2.
+  // Every pass starts at tile 0, so near its end the ring is refilled with
+  // tiles 0..3 of the next pass (seed pass -> sweep -> next block's seed).
   Ops o[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) load_ops(u, o[u]);
   floatx16 bq[2];
   bq[0] = bias(0);
   bq[1] = bias(1);
-  // one pass over all tiles; per_tile(acc, t) sees the logits of tile t
-  auto sweep = [&](auto&& per_tile) {
+  // one pass over tiles 0..len-1; per_tile(acc, t) sees the logits of tile t
+  auto sweep = [&](int len, auto&& per_tile) {
+    auto wrap = [&](int t) { return t >= len ? t - len : t; };   // t < 2 len
     floatx16 acc[2];
     acc[0] = logits(o[0], bq[0]);
     load_ops(wrap(4), o[0]);
     bq[0] = bias(2);
-    for (int t0 = 0; t0 < NT; t0 += 4) {
+    for (int t0 = 0; t0 < len; t0 += 4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = t0 + u;
-        const bool last = t == NT - 1;   // then tile t+1 is the next pass's tile 0 (discarded)
+        const bool last = t == len - 1;   // then tile t+1 is the next pass's tile 0 (discarded)
         acc[(u + 1) & 1] = logits(o[(u + 1) & 3], bq[(u + 1) & 1]);
         bq[(u + 1) & 1] = bias(last ? 0 : wrap(t + 3));
         load_ops(last ? 0 : wrap(t + 5), o[(u + 1) & 3]);
@@ -321,24 +406,25 @@ __device__ __forceinline__ void pc_consume(const PcArgs& pa, char* lds, int c, i
   };
   TwoPassState<KMAX> st;
   for (int jj = 0; jj < nj; ++jj) {
-    if (!pc_wait(full + c, jj + 1, abort_word, pa.spin_limit)) return;
+    if (!pc_wait(fl + kPcFull + c, jj + 1, abort_word, pa.spin_limit)) return;
 #pragma unroll
     for (int m = 0; m < R16; ++m) {
       zh[m] = *(const bf16x8*)(slot + m * 1024 + lane * 16);
       zl[m] = *(const bf16x8*)(slot + (R16 + m) * 1024 + lane * 16);
     }
     lds_drain();
-    freed[c] = jj + 1;
+    fl[kPcFreed + c] = jj + 1;
     st.init(a.k);
-    sweep([&](const floatx16& acc, int) { tp_pass1_tile<KMAX, FULL>(st, acc); });
+    sweep(P, [&](const floatx16& acc, int) { tp_pass1_tile<KMAX, FULL>(st, acc); });
     tp_threshold<KMAX>(st, hi, a.k);
-    sweep([&](const floatx16& acc, int t) {
-      tp_pass2_tile<KMAX, CAP>(st, acc, kTile * t + 4 * hf, lg, lane, a.perm, a.k);
+    sweep(NT, [&](const floatx16& acc, int t) {
+      tp_pass2_tile<KMAX, CAP, !FULL>(st, acc, t >= P, kTile * t + 4 * hf, lg, lane, perm, a.k);
     });
-    const long long b = (long long)blockIdx.x + (long long)(c + kPcCons * jj) * pa.G;
-    const long long n = b * kTile + (lane & 31);
-    tp_finish<KMAX, FULL>(st, lg, lane, hi, n < a.N, n, a.perm, a.k, a.out_idx, a.out_gate, a.out_logit,
-                          a.out_lse);
+    // the staging area must have been read out (block jj-1) before it is rewritten
+    if (!pc_wait(fl + kPcDrained + c, jj, abort_word, pa.spin_limit)) return;
+    tp_finish<KMAX, FULL>(st, lg, lane, hi, perm, a.k, a.out_logit != nullptr, stg);
+    lds_drain();
+    fl[kPcStaged + c] = jj + 1;
   }
 }
 
@@ -348,19 +434,35 @@ __global__ __launch_bounds__(64 * kPcWaves) void pc_kernel(PcArgs pa) {
   extern __shared__ __align__(16) char pc_lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // stage the bias (accumulator layout, -inf on padding rows); clear the counters
-  const int n4 = pa.base.NT * 8;
+  // stage the bias (accumulator layout, -inf on padding rows) and the sweep
+  // order (position -> expert, 16 bits: M <= 65535 here); clear the counters
+  const int mpad = pa.base.NT * kTile;
   const float4* src = (const float4*)pa.base.biasp;
   float4* dst = (float4*)(pc_lds + L::kBias);
-  for (int i = threadIdx.x; i < n4; i += 64 * kPcWaves) dst[i] = src[i];
-  if (threadIdx.x < L::kFlags / 4) ((int*)pc_lds)[threadIdx.x] = 0;
-  __syncthreads();
+  bool nz = false;   // any nonzero bias (padding rows hold -inf)
+  for (int i = threadIdx.x; i < mpad / 4; i += 64 * kPcWaves) {
+    const float4 v = src[i];
+    dst[i] = v;
+    nz = nz || (v.x != 0.f && v.x > -__builtin_inff()) || (v.y != 0.f && v.y > -__builtin_inff()) ||
+         (v.z != 0.f && v.z > -__builtin_inff()) || (v.w != 0.f && v.w > -__builtin_inff());
+  }
+  const int2* psrc = (const int2*)pa.base.perm;
+  uint32_t* pdst = (uint32_t*)(pc_lds + L::perm_off(mpad));
+  for (int i = threadIdx.x; i < mpad / 2; i += 64 * kPcWaves) {
+    const int2 v = psrc[i];
+    pdst[i] = ((uint32_t)v.x & 0xffffu) | ((uint32_t)v.y << 16);
+  }
+  if (threadIdx.x < kPcZOff / 4) ((int*)pc_lds)[threadIdx.x] = 0;
+  const bool has_bias = block_any(nz, (lds_i32*)pc_lds + kPcAnyBias);
   const int nbw = (pa.NB - (int)blockIdx.x + pa.G - 1) / pa.G;   // blocks of this workgroup
   if (wave < kPcProd)
     produce_z<R16, D, TAIL>(ProdArgs{pa.base.X, pa.base.N, pa.base.h, pa.R1q, pa.KSP, pa.G},
-                            PcHandOff<R16>{pc_lds, pa.spin_limit}, wave, lane, nbw);
+                            PcHandOff<KMAX, R16>{pc_lds, pa.spin_limit, pa.base.out_idx, pa.base.out_gate,
+                                                 pa.base.out_logit, FULL ? pa.base.out_lse : nullptr, pa.base.N,
+                                                 pa.base.k, pa.G, nbw},
+                            wave, lane, nbw);
   else
-    pc_consume<KMAX, FULL, R16>(pa, pc_lds, wave - kPcProd, lane, nbw);
+    pc_consume<KMAX, FULL, R16>(pa, pc_lds, wave - kPcProd, lane, nbw, has_bias);
 }
 
 }  // namespace more

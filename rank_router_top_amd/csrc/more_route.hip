@@ -88,6 +88,14 @@ bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, L
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Token scratch after the packed weights: z of every 32-token block for the
+// two-kernel path (bf16 storage, r <= 64).  0 where that path cannot run.
+size_t z_scratch_bytes(more_dtype dt, const Layout& L, int64_t N) {
+  if (dt != MORE_DT_BF16 || L.ksq <= 0 || L.r16 > 4 || N <= 0) return 0;
+  const int64_t nb = (N + kTile - 1) / kTile;
+  return align_up((size_t)nb * (size_t)z_block_bytes(L.r16));
+}
+
 more_status validate(int fullrank, more_dtype dt, const void* X, int64_t N, int64_t h,
                      const void* A, int64_t r, const void* B, int64_t M, const float* bias,
                      int32_t k, more_gate gate, const int32_t* idx, const float* gates,
@@ -116,11 +124,12 @@ more_status validate(int fullrank, more_dtype dt, const void* X, int64_t N, int6
 // every call) can restrict the candidates to a comma-separated subset of
 // "pc,slice,lock,stream,simple" -- a testing aid so that every path can be
 // checked on the shapes a faster one would take; "simple" always fits.
-enum { kPathPc = 1, kPathSlice = 2, kPathLock = 4, kPathStream = 8 };
+enum { kPathPc = 1, kPathSlice = 2, kPathLock = 4, kPathStream = 8, kPathSplit = 16 };
 bool path_allowed(int path) {
   const char* env = getenv("MORE_ROUTE_PATHS");
   if (!env || !*env) return true;
-  const char* name = path == kPathSlice ? "slice" : path == kPathPc ? "pc" : path == kPathLock ? "lock" : "stream";
+  const char* name = path == kPathSlice ? "slice" : path == kPathPc ? "pc" : path == kPathLock ? "lock"
+                     : path == kPathSplit ? "split" : "stream";
   const size_t len = strlen(name);
   for (const char* p = env; *p;) {
     const char* e = strchr(p, ',');
@@ -199,7 +208,6 @@ const char* more_status_str(more_status s) {
 
 size_t more_route_workspace_bytes(int fullrank, more_dtype dt, int64_t N, int64_t h, int64_t r,
                                   int64_t M, int32_t k, more_gate gate, int has_bias) {
-  (void)N;
   (void)has_bias;
   if (dt != MORE_DT_BF16 && dt != MORE_DT_F32) return 0;
   if (gate != MORE_GATE_TOPK_SOFTMAX && gate != MORE_GATE_FULL_SOFTMAX) return 0;
@@ -208,7 +216,8 @@ size_t more_route_workspace_bytes(int fullrank, more_dtype dt, int64_t N, int64_
   if (h > (1 << 20) || M > (1 << 24)) return 0;
   Layout L;
   make_layout(fullrank, dt, h, r, M, &L);
-  return L.total;
+  if (N < 0) return 0;
+  return L.total + (fullrank ? 0 : z_scratch_bytes(dt, L, N));
 }
 
 more_status more_lowrank_pack(more_dtype dt, const void* R1, int64_t h, int64_t r, const void* R2,
@@ -229,7 +238,7 @@ more_status more_lowrank_pack(more_dtype dt, const void* R1, int64_t h, int64_t 
 more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int64_t r,
                                       int64_t M, int32_t k, more_gate gate, int32_t* topk_idx,
                                       float* topk_gate, float* topk_logit, float* lse,
-                                      const void* workspace, size_t workspace_bytes, void* stream) {
+                                      void* workspace, size_t workspace_bytes, void* stream) {
   // R1/R2 are not read here; a non-null placeholder keeps the shared validation.
   more_status st = validate(0, dt, X, N, h, X, r, X, M, nullptr, k, gate, topk_idx, topk_gate,
                             topk_logit, lse);
@@ -238,7 +247,7 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   make_layout(0, dt, h, r, M, &L);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace % kAlign) != 0)
     return MORE_ERR_WORKSPACE;
-  const char* ws = (const char*)workspace;
+  char* ws = (char*)workspace;
   const bool full = gate == MORE_GATE_FULL_SOFTMAX;
   const int kmax = kmax_for(k);
   const int waves = waves_for(kmax);
@@ -258,6 +267,51 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   a.out_logit = topk_logit;
   a.out_lse = full ? lse : nullptr;
   const size_t shmem = (size_t)waves * log_bytes(kmax);
+  const size_t zbytes = z_scratch_bytes(dt, L, N);
+  if (zbytes > 0 && workspace_bytes >= L.total + zbytes && split_shape_ok(kmax, L.r16, L.Mpad) &&
+      path_allowed(kPathSplit)) {
+    // Two kernels: projection (R1 resident in LDS) writes z, routing sweeps it.
+    int ksp = 0;
+    bool tail = false;
+    proj_ksteps(h, L.r16, &ksp, &tail);
+    const size_t pj_lds = proj_lds_bytes(L.r16, ksp);
+    const size_t rt_lds = route_lds_bytes(kmax, L.Mpad);
+    if ((long long)pj_lds <= kLdsBytes && (long long)rt_lds <= kLdsBytes) {
+      proj_fn pf = pick_proj(L.r16, tail);
+      route_fn rf = pick_route(full, kmax, L.r16);
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          hipFuncSetAttribute((const void*)pf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pj_lds) !=
+              hipSuccess ||
+          hipFuncSetAttribute((const void*)rf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rt_lds) !=
+              hipSuccess)
+        return MORE_ERR_HIP;
+      const int64_t nb = (N + kTile - 1) / kTile;
+      if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
+      ProjArgs pa;
+      pa.X = X;
+      pa.N = N;
+      pa.h = (int)h;
+      pa.R1q = ws + L.off_r1q;
+      pa.KSQ = std::min(L.ksq, ksp);
+      pa.KSP = ksp;
+      pa.NB = (int)nb;
+      pa.Z = ws + L.total;
+      pa.spin_limit = 1 << 22;
+      const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kProjWaves - 1) / kProjWaves));
+      hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, (hipStream_t)stream, pa);
+      if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
+      RouteArgs ra;
+      ra.base = a;
+      ra.Z = pa.Z;
+      ra.NB = (int)nb;
+      ra.pre = std::min(L.NT, kPcSeedTiles);
+      const int64_t rg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kRouteWaves - 1) / kRouteWaves));
+      hipLaunchKernelGGL(rf, dim3((unsigned)rg), dim3(64 * kRouteWaves), rt_lds, (hipStream_t)stream, ra);
+      return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+    }
+  }
   const size_t pc_lds = (dt == MORE_DT_BF16 && L.ksq > 0) ? pc_lds_bytes(kmax, L.r16, L.Mpad) : 0;
   if (pc_lds > 0 && (long long)pc_lds <= kLdsBytes && path_allowed(kPathPc)) {
     // Producer/consumer kernel: one 12-wave workgroup per CU, persistent.
@@ -280,6 +334,7 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
     pa.KSP = L.ksq;
     pa.R1q = ws + L.off_r1q;
     pa.spin_limit = 1 << 22;
+    pa.pre = std::min(L.NT, kPcSeedTiles);
     hipLaunchKernelGGL(fn, dim3((unsigned)pa.G), dim3(64 * kPcWaves), pc_lds, (hipStream_t)stream, pa);
     return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
   }

@@ -109,6 +109,8 @@ struct SlHandOff {
     lds_drain();
     pc_flags(lds)[kSlFull + i % NZ] = i + 1;
   }
+  __device__ __forceinline__ bool retire(int, int) const { return true; }   // consumers store their own results
+  __device__ __forceinline__ void finish(int, int) const {}
 };
 
 // Barrier of the 8 consumer waves: arrive (release), then wait for `target`

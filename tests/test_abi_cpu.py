@@ -40,11 +40,17 @@ def test_version_and_status_strings():
 
 
 def test_workspace_size_is_pure_host_and_rejects_bad_args():
-    ws = R.workspace_bytes(False, R.MORE_DT_BF16, 262144, 2048, 32, 4096, 8, 0, True)
+    packed = R.workspace_bytes(False, R.MORE_DT_BF16, 0, 2048, 32, 4096, 8, 0, True)
     # packed R1 in two operand layouts (2 x 128 KiB) + packed R2 (256 KiB) + bias
     # operands + sweep order
-    assert 2 * 128 * 1024 + 256 * 1024 <= ws < 2 * 128 * 1024 + 256 * 1024 + 128 * 1024
-    assert ws % 256 == 0
+    assert 2 * 128 * 1024 + 256 * 1024 <= packed < 2 * 128 * 1024 + 256 * 1024 + 128 * 1024
+    # plus token scratch: z of every 32-token block as bf16 hi + lo (4 bytes per token and rank)
+    ws = R.workspace_bytes(False, R.MORE_DT_BF16, 262144, 2048, 32, 4096, 8, 0, True)
+    assert ws == packed + 262144 * 32 * 4
+    assert R.workspace_bytes(False, R.MORE_DT_BF16, 33, 2048, 32, 4096, 8, 0, True) == packed + 2 * 32 * 128
+    assert R.workspace_bytes(False, R.MORE_DT_F32, 1000, 2048, 32, 4096, 8, 0, True) == \
+        R.workspace_bytes(False, R.MORE_DT_F32, 0, 2048, 32, 4096, 8, 0, True)   # fp32: no two-kernel path
+    assert ws % 256 == 0 and packed % 256 == 0
     assert R.workspace_bytes(True, R.MORE_DT_BF16, 100, 2048, 0, 4096, 8, 0, True) >= 2048 * 4096 * 2
     assert R.workspace_bytes(False, R.MORE_DT_BF16, 1, 2048, 24, 4096, 8, 0, False) == 0   # r % 16
     assert R.workspace_bytes(False, R.MORE_DT_BF16, 1, 2044, 32, 4096, 8, 0, False) == 0   # h % 8

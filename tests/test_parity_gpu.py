@@ -258,13 +258,33 @@ PATH_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["slice", "pc", "lock", "stream", "none"])
+@pytest.mark.parametrize("path", ["split", "slice", "pc", "lock", "stream", "none"])
 @pytest.mark.parametrize("cfg,n,gate", PATH_CASES, ids=[f"{c.name}-{n}-g{g}" for c, n, g in PATH_CASES])
 def test_kernel_paths(oracle_lib, monkeypatch, path, cfg, n, gate):
     monkeypatch.setenv("MORE_ROUTE_PATHS", path)
     X = cfg.x_rows(0, 0, n, n_total=cfg.N)
     R1, R2, b = cfg.weights(0)
     check_lowrank(oracle_lib, X, R1, R2, b, cfg.k, gate, f"{cfg.name}-path-{path}")
+
+
+def test_packed_workspace_sizes(oracle_lib):
+    """Pack once, route batches of different sizes against one workspace: one
+    sized for the largest batch (the two-kernel path, token scratch present)
+    and one sized for no tokens at all (no scratch: a one-kernel path)."""
+    cfg = CF.HEADLINE
+    R1, R2, b = (R.to_device(a, DEV) for a in cfg.weights(0))
+    sizes = [1024 + 77, 300]
+    for n_ws in (max(sizes), 0):
+        nbytes = R.workspace_bytes(False, 0, n_ws, cfg.h, cfg.r, cfg.M, cfg.k, 0, True)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        R.pack_lowrank(R1, R2, b, ws)
+        for n in sizes:
+            say(f"packed workspace for {n_ws} tokens, batch of {n}")
+            Xn = cfg.x_rows(0, 0, n, n_total=cfg.N)
+            g = to_np(R.route_lowrank_packed(R.to_device(Xn, DEV), cfg.r, cfg.M, cfg.k, 0, ws))
+            torch.cuda.synchronize()
+            o = oracle_lib.route_lowrank(Xn, *cfg.weights(0), cfg.k, 0)
+            compare(o, g, cfg.k, False, 2e-4, f"packed-{n_ws}-{n}")
 
 
 def test_ties_many_experts(oracle_lib):
