@@ -7,9 +7,11 @@ A step is one full routing call (more_route_lowrank: sweep-order/weight packing
 kernel + the fused router kernel) over one batch of synthetic tokens already
 resident in HBM.  Prints ONE JSON line:
   value          routed tokens/s = N / mean step time
-  roofline       the fused router kernel alone, timed with HIP events on its
-                 stream: algorithmic bytes (X + outputs + weights) per launch
-                 over its mean duration, against the 8 TB/s HBM peak
+  roofline       the routing call alone (weights packed once: the projection
+                 kernel streaming X, then the routing kernel), timed with HIP
+                 events on its stream: algorithmic bytes (X + outputs +
+                 weights) per call over its mean duration, against the 8 TB/s
+                 HBM peak
   pct_roofline   roofline time / step time, roofline time = max(X bytes / 8 TB/s,
                  2N(hr + rM) / 2.5 PFLOP/s)
   cpu_baseline   the fp64 oracle on a bounded sample of the same tokens, timed
@@ -30,8 +32,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
-# the fused router kernel the headline workload dispatches to (rocprofv3 name)
-KERNEL_NAME = "more::pc_kernel<8, false, 2, 8, false>"
+# the kernels one routing call of the headline workload runs (rocprofv3 names)
+ROUTER_KERNELS = ("more::proj_kernel<2, 8, false, 4>", "more::route_kernel<8, false, 2, 8>")
+KERNEL_NAME = " + ".join(ROUTER_KERNELS)
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published (no sparsity)
 CONTEXT = {
     "source": "MoRE: Scaling mixture of experts with hardware-aware low-rank routing (B200, bf16)",
@@ -81,9 +84,9 @@ def source_hash():
 
 
 def read_counter(run_dir, counter):
-    """Per-dispatch mean of `counter` (KiB) for the router kernel and the copy
+    """Per-dispatch mean of `counter` (KiB) for each router kernel and the copy
     kernel in a rocprofv3 --pmc CSV (rows are per dimension instance; summed
-    per dispatch)."""
+    per dispatch).  "router" is the sum over the kernels of one routing call."""
     import csv
     import glob
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
@@ -96,13 +99,13 @@ def read_counter(run_dir, counter):
                 if row["Counter_Name"] != counter:
                     continue
                 name = row["Kernel_Name"]
-                kind = "router" if KERNEL_NAME.split("<")[0] in name else (
+                kind = next((kn for kn in ROUTER_KERNELS if kn in name), None) or (
                     "copy" if "copyBuffer" in name else None)
                 if kind:
                     key = (kind, row["Dispatch_Id"])
                     per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
     out = {}
-    for kind in ("router", "copy"):
+    for kind in ROUTER_KERNELS + ("copy",):
         vals = [v for (k, _), v in per.items() if k == kind]
         if kind == "copy" and vals:
             # the calibration copies (256 MiB) are the large ones; the runtime
@@ -111,6 +114,7 @@ def read_counter(run_dir, counter):
         if not vals:
             raise SystemExit(f"no {kind} dispatches with {counter} in {run_dir}")
         out[kind] = (sum(vals) / len(vals), len(vals))
+    out["router"] = (sum(out[kn][0] for kn in ROUTER_KERNELS), min(out[kn][1] for kn in ROUTER_KERNELS))
     return out
 
 
@@ -130,6 +134,8 @@ def write_traffic(args):
            "algorithmic_bytes": alg, "traffic_over_algorithmic": (fb + wb) / alg,
            "fetch_factor": f_fac, "write_factor": w_fac,
            "router_dispatches": [fetch["router"][1], write["router"][1]],
+           "per_kernel_fetch_bytes": {kn: fetch[kn][0] * 1024.0 * f_fac for kn in ROUTER_KERNELS},
+           "per_kernel_write_bytes": {kn: write[kn][0] * 1024.0 * w_fac for kn in ROUTER_KERNELS},
            "copy_bytes": copy_bytes}
     path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
     with open(path, "w") as f:
@@ -218,7 +224,7 @@ def main():
     ms_step = (t_end - t_start) * 1e3 / args.steps
     log(f"step {ms_step:.4f} ms")
 
-    # the fused router kernel alone (weights packed once, as for static weights)
+    # the routing call alone (weights packed once, as for static weights)
     R.pack_lowrank(R1, R2, b, ws, stream=stream)
 
     def kernel_only():
@@ -232,7 +238,7 @@ def main():
         R.pack_lowrank(R1, R2, b, ws, stream=stream)
 
     p_mean = time_events(torch, pack_only, 20, stream)[0]
-    log(f"router kernel mean {k_mean:.4f} ms (p10 {k_p10:.4f}, p90 {k_p90:.4f}); pack {p_mean:.4f} ms")
+    log(f"routing call mean {k_mean:.4f} ms (p10 {k_p10:.4f}, p90 {k_p90:.4f}); pack {p_mean:.4f} ms")
 
     alg_bytes = algorithmic_bytes(cfg, cfg.k, False)
     achieved = alg_bytes / (k_mean * 1e-3) / 1e9

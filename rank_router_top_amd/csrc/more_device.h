@@ -37,6 +37,16 @@ typedef __attribute__((address_space(3))) floatx4 lds_f4;
 typedef __attribute__((address_space(3))) const char lds_cchar;
 typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
 typedef __attribute__((address_space(3))) const bf16x8 lds_cbf16x8;
+// Wait until every LDS (and scalar-memory) operation of the wave has completed.
+// The s_waitcnt builtin (lgkmcnt(0), vmcnt and expcnt at their maxima) is an
+// instruction the compiler's own wait-count tracking sees, so it knows the
+// counter is empty afterwards; the empty asm keeps memory accesses from
+// moving across it.
+__device__ __forceinline__ void lds_drain() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup-wide OR of v through one LDS word (no static LDS; two barriers).
 __device__ __forceinline__ bool block_any(bool v, lds_i32* word) {
   if (threadIdx.x == 0) *word = 0;

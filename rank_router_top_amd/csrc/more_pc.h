@@ -99,7 +99,6 @@ template <int AUX = 0>
 __device__ __forceinline__ bf16x8 buf_load(rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
 }
-__device__ __forceinline__ void lds_drain() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // The hand-off counters are addressed explicitly in the LDS address space: a
 // volatile access through a generic pointer becomes a FLAT instruction, which

@@ -196,9 +196,14 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
       for (int rb = 0; rb < R16; ++rb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[g][rb][v] = 0.f;
-    bf16x8 rr[2][R16];
+    // down-projection operands: a ring of RP K-steps read from LDS RP-1 steps ahead
+    constexpr int RP = 4;
+    static_assert(D % RP == 0, "the LDS operand ring must divide the X ring");
+    bf16x8 rr[RP][R16];
 #pragma unroll
-    for (int rb = 0; rb < R16; ++rb) rr[0][rb] = r1op(0, rb);
+    for (int q = 0; q + 1 < RP; ++q)
+#pragma unroll
+      for (int rb = 0; rb < R16; ++rb) rr[q][rb] = r1op(q < pa.KSP ? q : pa.KSP - 1, rb);
     for (int sb = 0; sb < NBAT; ++sb) {
       const bool last = sb == NBAT - 1;   // refill with the next block's first K-steps
       const rsrc_t xd = make_rsrc(last ? nbase : cbase, last ? nbytes : cbytes);
@@ -206,15 +211,14 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
         const int s = sb * D + u;
-        // down-projection operands of the next K-step (LDS, one step ahead)
-        const int sn = (s + 1 < pa.KSP) ? s + 1 : s;
+        const int sn = (s + RP - 1 < pa.KSP) ? s + RP - 1 : pa.KSP - 1;
 #pragma unroll
-        for (int rb = 0; rb < R16; ++rb) rr[(u + 1) & 1][rb] = r1op(sn, rb);
+        for (int rb = 0; rb < R16; ++rb) rr[(u + RP - 1) % RP][rb] = r1op(sn, rb);
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
           for (int rb = 0; rb < R16; ++rb)
-            acc[g][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rr[u & 1][rb], xr[u][g], acc[g][rb], 0, 0, 0);
+            acc[g][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rr[u % RP][rb], xr[u][g], acc[g][rb], 0, 0, 0);
         issue(u, xd, s0 + u);
         // slot order: the MFMAs of slot u wait only for slot u's loads
         __builtin_amdgcn_sched_barrier(0);

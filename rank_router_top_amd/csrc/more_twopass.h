@@ -167,6 +167,7 @@ __device__ __forceinline__ void tp_pass2_log(TwoPassState<KMAX>& st, const float
         }
       }
     }
+    lds_drain();   // as in tp_pass2_groups: keep the LDS counter uniform after the branch
   }
 }
 
@@ -288,6 +289,11 @@ __device__ __forceinline__ void tp_pass2_groups(TwoPassState<KMAX>& st, const fl
         st.cnt += (g[q] >= st.thr) ? 1 : 0;
       }
     }
+    // Let the appends complete here: LDS operations share one in-order
+    // counter, and with a varying number of them in flight after this branch
+    // every later wait for a prefetched operand (the bias) would have to
+    // assume the worst case and wait for the appends as well.
+    lds_drain();
   }
 }
 
@@ -425,6 +431,7 @@ __device__ __forceinline__ void tp_finish_groups(const TwoPassState<KMAX>& st, G
   float L[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) L[j] = (j < KMAX - k) ? __builtin_inff() : kLowest;
+#pragma unroll 2
   for (int c = 0; c < st.cnt; ++c) {
     const floatx4 v = lg.val[c * kWave + lane];
 #pragma unroll
@@ -443,32 +450,30 @@ __device__ __forceinline__ void tp_finish_groups(const TwoPassState<KMAX>& st, G
   //    a logit's rank is the number of selected logits above it: each half
   //    writes the expert index of its own selected logits straight into the
   //    token's result row.  Otherwise (rare) an exact merge orders them.
+  const int tok = lane & 31;
+  const int o = tok * k;
+  // rank-writes (valid only without ties; the slow path rewrites every rank)
   int nge = 0;
+#pragma unroll 2
   for (int c = 0; c < st.cnt; ++c) {
     const floatx4 v = lg.val[c * kWave + lane];
+    const int p = lg.pos[c * kWave + lane];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) nge += v[e] >= vk ? 1 : 0;
+    for (int e = 0; e < 4; ++e) {
+      if (v[e] >= vk) {
+        ++nge;
+        int r = -(KMAX - k);   // the +inf pads count as larger
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) r += T[j] > v[e] ? 1 : 0;
+        if (r < k) stg[S::kIdx + o + r] = __int_as_float((int)perm[p + e]);
+      }
+    }
   }
   bool tie = nge + (int)partner_u32((uint32_t)nge, hi_half) != k;
 #pragma unroll
   for (int j = 0; j + 1 < KMAX; ++j) tie = tie || (j >= KMAX - k && T[j] == T[j + 1]);
-  const int tok = lane & 31;
-  const int o = tok * k;
   float V[KMAX];
   if (!any_lane(tie)) {
-    for (int c = 0; c < st.cnt; ++c) {
-      const floatx4 v = lg.val[c * kWave + lane];
-      const int p = lg.pos[c * kWave + lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (v[e] >= vk) {
-          int r = -(KMAX - k);   // the +inf pads count as larger
-#pragma unroll
-          for (int j = 0; j < KMAX; ++j) r += T[j] > v[e] ? 1 : 0;
-          stg[S::kIdx + o + r] = __int_as_float((int)perm[p + e]);
-        }
-      }
-    }
     if (hi_half) return;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) V[j] = T[(j + KMAX - k) < KMAX ? (j + KMAX - k) : KMAX - 1];
