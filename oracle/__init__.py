@@ -7,12 +7,16 @@ calls or links anything here.
 Method: "MoRE: Scaling mixture of experts with hardware-aware low-rank routing",
 §2 (standard and low-rank router), App. F eq. (5) (logits), App. F.1
 Algorithm 1 and Fig. 12 (exact top-k, softmax over the k selected logits),
-App. F.2.1 eq. (6) (full softmax / log-sum-exp).  The arithmetic lives in
+App. F.2.1 eq. (6) (full softmax / log-sum-exp), eq. (7) and (9) (column sums
+of the full softmax and the Switch balancing loss), App. G.1 (normalised
+routing entropy).  The arithmetic lives in
 ``more_oracle.c`` (plain C, fp64, OpenMP over tokens); this module only builds
 it with gcc and marshals numpy arrays through ctypes.
 """
-from .oracle import (DT_BF16, DT_F32, DT_F64, GATE_FULL, GATE_TOPK, build, library_path,
-                     logits, max_threads, route_fullrank, route_lowrank)
+from .oracle import (DT_BF16, DT_F32, DT_F64, GATE_FULL, GATE_TOPK, balance_lowrank, balance_stats,
+                     build, library_path, logits, max_threads, route_fullrank, route_lowrank,
+                     softmax_colsum)
 
-__all__ = ["DT_BF16", "DT_F32", "DT_F64", "GATE_FULL", "GATE_TOPK", "build", "library_path",
-           "logits", "max_threads", "route_fullrank", "route_lowrank"]
+__all__ = ["DT_BF16", "DT_F32", "DT_F64", "GATE_FULL", "GATE_TOPK", "balance_lowrank", "balance_stats",
+           "build", "library_path", "logits", "max_threads", "route_fullrank", "route_lowrank",
+           "softmax_colsum"]

@@ -33,6 +33,9 @@
  *      lse = m + log Z, g_j = exp(l_j - lse).
  *   5. side outputs: the k selected logits, l_(k), l_(k+1) (-inf if k = M)
  *      and max_j |l_j|, the data of the gap rule used to compare against.
+ * Balancing statistics (App. F.2.1, eq. (7)): psum_i = sum over tokens of the
+ * full-softmax probability P_{n,i} = exp(l_{n,i} - m_n) / Z_n of eq. (6),
+ * with m_n and Z_n taken over all M experts of the biased logits.
  * No blocking, fusion or reordering beyond these definitions.
  */
 #include <math.h>
@@ -215,6 +218,66 @@ int oracle_logits(int dt, const void* X, int64_t N, int64_t h, const void* A, in
     for (int64_t n = 0; n < N; ++n) token_logits(dt, X, n, h, A, r, B, M, bias, fullrank, x, z, out + n * M);
     free(x);
     free(z);
+    return OR_OK;
+}
+
+/*
+ * Column sums of the row-wise full softmax (eq. (6), (7)): psum[i] = sum_n
+ * P_{n,i}.  Per token: logits as above, m = max l, Z = sum exp(l - m),
+ * P = exp(l - m) / Z; each thread sums its tokens, the thread sums are added
+ * at the end.
+ */
+int oracle_softmax_colsum(int dt, const void* X, int64_t N, int64_t h, const void* A, int64_t r,
+                          const void* B, int64_t M, const float* bias, int fullrank, double* psum_out,
+                          int nthreads) {
+    if (dt < OR_DT_BF16 || dt > OR_DT_F64 || !X || !A || (!fullrank && !B) || !psum_out) return OR_ERR_ARG;
+    if (N < 0 || h < 1 || M < 1 || (!fullrank && r < 1)) return OR_ERR_ARG;
+    if (!all_finite(dt, X, N * h) || !all_finite(dt, A, fullrank ? h * M : h * r) ||
+        (!fullrank && !all_finite(dt, B, r * M)) || (bias && !all_finite(OR_DT_F32, bias, M)))
+        return OR_ERR_NONFINITE;
+    int T = 1;
+#ifdef _OPENMP
+    T = nthreads > 0 ? nthreads : omp_get_max_threads();
+#endif
+    (void)nthreads;
+    const size_t zr = (size_t)(r > 0 ? r : 1);
+    double* part = (double*)calloc((size_t)T * (size_t)M, sizeof(double));
+    double* xs = (double*)malloc(sizeof(double) * (size_t)T * (size_t)h);
+    double* zs = (double*)malloc(sizeof(double) * (size_t)T * zr);
+    double* ls = (double*)malloc(sizeof(double) * (size_t)T * (size_t)M);
+    if (!part || !xs || !zs || !ls) {
+        free(part);
+        free(xs);
+        free(zs);
+        free(ls);
+        return OR_ERR_NOMEM;
+    }
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(T) schedule(static)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        int t = 0;
+#ifdef _OPENMP
+        t = omp_get_thread_num();
+#endif
+        double* l = ls + (size_t)t * (size_t)M;
+        double* acc = part + (size_t)t * (size_t)M;
+        token_logits(dt, X, n, h, A, r, B, M, bias, fullrank, xs + (size_t)t * (size_t)h, zs + (size_t)t * zr, l);
+        double m = l[0];
+        for (int64_t i = 1; i < M; ++i) m = l[i] > m ? l[i] : m;
+        double Z = 0.0;
+        for (int64_t i = 0; i < M; ++i) Z += exp(l[i] - m);
+        for (int64_t i = 0; i < M; ++i) acc[i] += exp(l[i] - m) / Z;
+    }
+    for (int64_t i = 0; i < M; ++i) {
+        double s = 0.0;
+        for (int t = 0; t < T; ++t) s += part[(size_t)t * (size_t)M + (size_t)i];
+        psum_out[i] = s;
+    }
+    free(part);
+    free(xs);
+    free(zs);
+    free(ls);
     return OR_OK;
 }
 

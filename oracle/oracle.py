@@ -49,7 +49,9 @@ def _load():
         lib.oracle_route_fullrank.argtypes = [i32, p, i64, i64, p, i64, p, i32, i32,
                                               p, p, p, p, p, p, p, i32]
         lib.oracle_logits.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, p]
-        for f in (lib.oracle_route_lowrank, lib.oracle_route_fullrank, lib.oracle_logits):
+        lib.oracle_softmax_colsum.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, p, i32]
+        for f in (lib.oracle_route_lowrank, lib.oracle_route_fullrank, lib.oracle_logits,
+                  lib.oracle_softmax_colsum):
             f.restype = C.c_int
         lib.oracle_max_threads.restype = C.c_int
         _lib = lib
@@ -131,6 +133,59 @@ def logits(X, A, B, bias, fullrank: bool = False) -> np.ndarray:
     out = np.empty((N, M), np.float64)
     _check(_load().oracle_logits(dt, _ptr(X), N, h, _ptr(A), r, _ptr(None if fullrank else B), M,
                                  _ptr(b), int(fullrank), _ptr(out)))
+    return out
+
+
+def softmax_colsum(X, A, B, bias, fullrank: bool = False, nthreads: int = 0) -> np.ndarray:
+    """psum_i = sum over tokens of the full-softmax probability of expert i (eq. 6, 7)."""
+    X, A = np.ascontiguousarray(X), np.ascontiguousarray(A)
+    dt = _dt_code(X)
+    N, h = X.shape
+    if fullrank:
+        M, r = A.shape[1], 0
+    else:
+        B = np.ascontiguousarray(B)
+        r, M = B.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty(M, np.float64)
+    _check(_load().oracle_softmax_colsum(dt, _ptr(X), N, h, _ptr(A), r, _ptr(None if fullrank else B), M,
+                                         _ptr(b), int(fullrank), _ptr(out), nthreads))
+    return out
+
+
+def balance_stats(psum, counts, N: int, k: int) -> tuple[float, float]:
+    """Switch balancing loss (eq. 9) and normalised routing entropy (App. G.1).
+
+    L_bal = M * sum_i f_i p_i with f_i = counts_i / (N k) (the share of the
+    N k dispatch slots) and p_i = psum_i / N.  H_norm = -sum_a q_a log q_a /
+    log M with q_a = counts_a / sum_b counts_b and 0 log 0 = 0; for M = 1
+    (one expert carries everything, which is also an even load) H_norm = 1.
+    """
+    psum = np.asarray(psum, np.float64)
+    counts = np.asarray(counts, np.int64)
+    M = psum.shape[0]
+    f = counts.astype(np.float64) / (N * k)
+    p = psum / N
+    lbal = float(M * np.dot(f, p))
+    if M == 1:
+        return lbal, 1.0
+    q = counts[counts > 0].astype(np.float64) / counts.sum()
+    return lbal, float(-(q * np.log(q)).sum() / np.log(M))
+
+
+def balance_lowrank(X, R1, R2, bias, k: int, gate: int = GATE_TOPK, nthreads: int = 0) -> dict:
+    """Training-forward outputs (App. F.2.1, Algorithm 2 and eq. 7, 9): the
+    routing results of route_lowrank, plus psum (eq. 7), the dispatch counts
+    per expert (bincount of the selected indices) and (L_bal, H_norm)."""
+    out = route_lowrank(X, R1, R2, bias, k, gate, nthreads)
+    # lse of every token (the full-softmax normaliser is an output of the training forward)
+    full = route_lowrank(X, R1, R2, bias, k, GATE_FULL, nthreads) if gate != GATE_FULL else out
+    out["lse"] = full["lse"]
+    N = X.shape[0]
+    M = R2.shape[1]
+    out["psum"] = softmax_colsum(X, R1, R2, bias, False, nthreads)
+    out["counts"] = np.bincount(out["idx"].reshape(-1), minlength=M).astype(np.int64)
+    out["lbal"], out["hnorm"] = balance_stats(out["psum"], out["counts"], N, k) if N > 0 else (0.0, 0.0)
     return out
 
 
