@@ -138,6 +138,46 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Training forward with balancing statistics (App. F.2.1, Algorithm 2: a
+ * first sweep with the running top-k and the running maximum / normaliser of
+ * eq. (8), then a second sweep that recomputes every logit tile and adds the
+ * full-softmax probabilities into per-expert column sums; eq. (7) and (9);
+ * App. G.1 for the entropy).  Against weights packed by more_lowrank_pack:
+ *   topk_idx, topk_gate, topk_logit  as for more_lowrank_route_packed.
+ *   lse        N fp32 (required): log sum over all M experts of exp(l), in
+ *              both gate modes (the training forward's normaliser m + log Z).
+ *   psum       M fp32 (required): psum_i = sum over the N tokens of
+ *              P_{n,i} = exp(l_{n,i} - lse_n), the biased logits' softmax.
+ *   counts     M int32 (required): how many of the N k selected slots went to
+ *              each expert (a bincount of topk_idx).
+ *   stats      2 fp32 (required): stats[0] = L_bal = M sum_i f_i p_i with
+ *              f_i = counts_i / (N k) and p_i = psum_i / N (the Switch loss,
+ *              eq. 9); stats[1] = H_norm = -sum_a q_a log q_a / log M with
+ *              q_a = counts_a / (N k) (1 for M = 1).
+ *   workspace  at least more_balance_workspace_bytes(...) bytes: the packed
+ *              weights, then the token scratch and the per-slot partial sums
+ *              (overwritten).
+ * Envelope: the shapes whose routing runs as the projection + routing
+ * kernel pair: bf16, k <= 8, M <= 5888 (M <= 14720 for k <= 4), and R1 small
+ * enough to stay in the projection kernel's LDS (h <= 4608 for r = 16,
+ * h <= 2048 for r = 32, h <= 768 for r = 48 or 64); other shapes return
+ * MORE_ERR_UNSUPPORTED (more_balance_workspace_bytes returns 0 for them).  psum, counts and stats are written in a fixed
+ * summation order (the same inputs give the same bits).  N = 0 is a no-op.
+ */
+more_status more_lowrank_balance_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int64_t r,
+                                        int64_t M, int32_t k, more_gate gate, int32_t* topk_idx,
+                                        float* topk_gate, float* topk_logit, float* lse, float* psum,
+                                        int32_t* counts, float* stats, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes of more_lowrank_balance_packed for these arguments (0 where
+ * it would return MORE_ERR_UNSUPPORTED or reject the shape).  Pure host
+ * function, no HIP call.
+ */
+size_t more_balance_workspace_bytes(more_dtype dt, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k);
+
+/*
  * Fused standard (full-rank) router + top-k + gates: the same selection and
  * gates with l = x W + b (§2 standard router; App. H.3 Fig. 20 fuses it the
  * same way, reloading weight tiles instead of a rank-r intermediate).

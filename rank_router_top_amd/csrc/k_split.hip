@@ -17,17 +17,18 @@ size_t proj_lds_bytes(int r16, int ksp) {
     default: return PjLds<4, kProjWaves>::bytes(ksp);
   }
 }
-template <bool FULL, int KMAX>
+template <bool FULL, bool LSE, int KMAX>
 static route_fn route_r(int r16) {
   switch (r16) {
-    case 1: return route_kernel<KMAX, FULL, 1, kRouteWaves>;
-    case 2: return route_kernel<KMAX, FULL, 2, kRouteWaves>;
-    default: return route_kernel<KMAX, FULL, 4, kRouteWaves>;
+    case 1: return route_kernel<KMAX, FULL, 1, kRouteWaves, LSE>;
+    case 2: return route_kernel<KMAX, FULL, 2, kRouteWaves, LSE>;
+    default: return route_kernel<KMAX, FULL, 4, kRouteWaves, LSE>;
   }
 }
-route_fn pick_route(bool full, int kmax, int r16) {
-  if (full) return kmax <= 4 ? route_r<true, 4>(r16) : route_r<true, 8>(r16);
-  return kmax <= 4 ? route_r<false, 4>(r16) : route_r<false, 8>(r16);
+route_fn pick_route(bool full, bool lse, int kmax, int r16) {
+  if (full) return kmax <= 4 ? route_r<true, true, 4>(r16) : route_r<true, true, 8>(r16);
+  if (lse) return kmax <= 4 ? route_r<false, true, 4>(r16) : route_r<false, true, 8>(r16);
+  return kmax <= 4 ? route_r<false, false, 4>(r16) : route_r<false, false, 8>(r16);
 }
 size_t route_lds_bytes(int kmax, long long mpad) {
   return kmax <= 4 ? RouteLds<4>::bytes(kRouteWaves, mpad) : RouteLds<8>::bytes(kRouteWaves, mpad);

@@ -74,7 +74,8 @@ constexpr bool split_shape_ok(int kmax, int r16, long long mpad) {
   return kmax <= 8 && r16 <= 4 && mpad <= 65535;
 }
 proj_fn pick_proj(int r16, bool tail);
-route_fn pick_route(bool full, int kmax, int r16);
+// lse: pass 1 over every tile and lse written (the full-softmax gate implies it).
+route_fn pick_route(bool full, bool lse, int kmax, int r16);
 size_t route_lds_bytes(int kmax, long long mpad);
 size_t proj_lds_bytes(int r16, int ksp);
 

@@ -19,6 +19,7 @@
 #include "more_device.h"
 #include "more_pack.h"
 #include "more_dispatch.h"
+#include "more_balance.h"
 
 using namespace more;
 
@@ -96,6 +97,16 @@ size_t z_scratch_bytes(more_dtype dt, const Layout& L, int64_t N) {
   return align_up((size_t)nb * (size_t)z_block_bytes(L.r16));
 }
 
+// Workspace of the balancing call: packed weights, z scratch for N tokens,
+// then the per-slot partial column sums (fp32, by sweep position) and the
+// per-slot counts (int32, by expert).  Returns false outside its envelope
+// (bf16, r <= 64, k <= 8, the two-kernel path's shape limits).
+struct BalLayout {
+  size_t off_z, off_part, off_cpart, total;
+  int slots;
+};
+bool balance_layout(more_dtype dt, const Layout& L, int64_t N, int64_t h, int64_t M, int32_t k, BalLayout* B);
+
 more_status validate(int fullrank, more_dtype dt, const void* X, int64_t N, int64_t h,
                      const void* A, int64_t r, const void* B, int64_t M, const float* bias,
                      int32_t k, more_gate gate, const int32_t* idx, const float* gates,
@@ -139,6 +150,69 @@ bool path_allowed(int path) {
     p = e + 1;
   }
   return false;
+}
+
+// Whether the two-kernel path has an instance for this shape (LDS included).
+bool split_fits(int kmax, const Layout& L, int64_t h) {
+  if (!split_shape_ok(kmax, L.r16, L.Mpad)) return false;
+  int ksp = 0;
+  bool tail = false;
+  proj_ksteps(h, L.r16, &ksp, &tail);
+  return (long long)proj_lds_bytes(L.r16, ksp) <= kLdsBytes && (long long)route_lds_bytes(kmax, L.Mpad) <= kLdsBytes;
+}
+
+// Two kernels: projection (R1 resident in LDS) writes z of every 32-token
+// block to the token scratch behind the packed weights, routing sweeps it.
+// lse_mode: pass 1 covers every tile and lse is written (implied by full).
+more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int kmax, bool full, bool lse_mode,
+                         char* ws, hipStream_t stream) {
+  int ksp = 0;
+  bool tail = false;
+  proj_ksteps(h, L.r16, &ksp, &tail);
+  const size_t pj_lds = proj_lds_bytes(L.r16, ksp);
+  const size_t rt_lds = route_lds_bytes(kmax, L.Mpad);
+  proj_fn pf = pick_proj(L.r16, tail);
+  route_fn rf = pick_route(full, lse_mode, kmax, L.r16);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipFuncSetAttribute((const void*)pf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pj_lds) != hipSuccess ||
+      hipFuncSetAttribute((const void*)rf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rt_lds) != hipSuccess)
+    return MORE_ERR_HIP;
+  const int64_t nb = (a.N + kTile - 1) / kTile;
+  if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
+  ProjArgs pa;
+  pa.X = a.X;
+  pa.N = a.N;
+  pa.h = (int)h;
+  pa.R1q = ws + L.off_r1q;
+  pa.KSQ = std::min(L.ksq, ksp);
+  pa.KSP = ksp;
+  pa.NB = (int)nb;
+  pa.Z = ws + L.total;
+  pa.spin_limit = 1 << 22;
+  const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kProjWaves - 1) / kProjWaves));
+  hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, stream, pa);
+  if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
+  RouteArgs ra;
+  ra.base = a;
+  ra.Z = pa.Z;
+  ra.NB = (int)nb;
+  ra.pre = std::min(L.NT, kPcSeedTiles);
+  const int64_t rg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kRouteWaves - 1) / kRouteWaves));
+  hipLaunchKernelGGL(rf, dim3((unsigned)rg), dim3(64 * kRouteWaves), rt_lds, stream, ra);
+  return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+}
+
+bool balance_layout(more_dtype dt, const Layout& L, int64_t N, int64_t h, int64_t M, int32_t k, BalLayout* B) {
+  if (dt != MORE_DT_BF16 || L.ksq <= 0 || L.r16 > 4 || k > 8 || !split_fits(kmax_for(k), L, h)) return false;
+  const int64_t nb = N > 0 ? (N + kTile - 1) / kTile : 0;
+  B->slots = (int)std::min<int64_t>(kBalSlots, std::max<int64_t>(nb, 1));
+  B->off_z = L.total;
+  B->off_part = B->off_z + z_scratch_bytes(dt, L, N);
+  B->off_cpart = B->off_part + align_up((size_t)B->slots * (size_t)L.Mpad * sizeof(float));
+  B->total = B->off_cpart + align_up((size_t)B->slots * (size_t)M * sizeof(int));
+  return true;
 }
 
 lowrank_fn pick_lowrank(more_dtype dt, bool full, int kmax, int r16) {
@@ -268,50 +342,8 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   a.out_lse = full ? lse : nullptr;
   const size_t shmem = (size_t)waves * log_bytes(kmax);
   const size_t zbytes = z_scratch_bytes(dt, L, N);
-  if (zbytes > 0 && workspace_bytes >= L.total + zbytes && split_shape_ok(kmax, L.r16, L.Mpad) &&
-      path_allowed(kPathSplit)) {
-    // Two kernels: projection (R1 resident in LDS) writes z, routing sweeps it.
-    int ksp = 0;
-    bool tail = false;
-    proj_ksteps(h, L.r16, &ksp, &tail);
-    const size_t pj_lds = proj_lds_bytes(L.r16, ksp);
-    const size_t rt_lds = route_lds_bytes(kmax, L.Mpad);
-    if ((long long)pj_lds <= kLdsBytes && (long long)rt_lds <= kLdsBytes) {
-      proj_fn pf = pick_proj(L.r16, tail);
-      route_fn rf = pick_route(full, kmax, L.r16);
-      int dev = 0, cus = 0;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-          hipFuncSetAttribute((const void*)pf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pj_lds) !=
-              hipSuccess ||
-          hipFuncSetAttribute((const void*)rf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rt_lds) !=
-              hipSuccess)
-        return MORE_ERR_HIP;
-      const int64_t nb = (N + kTile - 1) / kTile;
-      if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
-      ProjArgs pa;
-      pa.X = X;
-      pa.N = N;
-      pa.h = (int)h;
-      pa.R1q = ws + L.off_r1q;
-      pa.KSQ = std::min(L.ksq, ksp);
-      pa.KSP = ksp;
-      pa.NB = (int)nb;
-      pa.Z = ws + L.total;
-      pa.spin_limit = 1 << 22;
-      const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kProjWaves - 1) / kProjWaves));
-      hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, (hipStream_t)stream, pa);
-      if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
-      RouteArgs ra;
-      ra.base = a;
-      ra.Z = pa.Z;
-      ra.NB = (int)nb;
-      ra.pre = std::min(L.NT, kPcSeedTiles);
-      const int64_t rg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kRouteWaves - 1) / kRouteWaves));
-      hipLaunchKernelGGL(rf, dim3((unsigned)rg), dim3(64 * kRouteWaves), rt_lds, (hipStream_t)stream, ra);
-      return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
-    }
-  }
+  if (zbytes > 0 && workspace_bytes >= L.total + zbytes && split_fits(kmax, L, h) && path_allowed(kPathSplit))
+    return launch_split(a, L, h, kmax, full, full, ws, (hipStream_t)stream);
   const size_t pc_lds = (dt == MORE_DT_BF16 && L.ksq > 0) ? pc_lds_bytes(kmax, L.r16, L.Mpad) : 0;
   if (pc_lds > 0 && (long long)pc_lds <= kLdsBytes && path_allowed(kPathPc)) {
     // Producer/consumer kernel: one 12-wave workgroup per CU, persistent.
@@ -429,6 +461,92 @@ more_status more_route_lowrank(more_dtype dt, const void* X, int64_t N, int64_t 
   if (st != MORE_OK) return st;
   return more_lowrank_route_packed(dt, X, N, h, r, M, k, gate, topk_idx, topk_gate, topk_logit, lse,
                                    workspace, workspace_bytes, stream);
+}
+
+size_t more_balance_workspace_bytes(more_dtype dt, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k) {
+  if (more_route_workspace_bytes(0, dt, N, h, r, M, k, MORE_GATE_TOPK_SOFTMAX, 0) == 0) return 0;
+  Layout L;
+  make_layout(0, dt, h, r, M, &L);
+  BalLayout B;
+  return balance_layout(dt, L, N, h, M, k, &B) ? B.total : 0;
+}
+
+more_status more_lowrank_balance_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int64_t r,
+                                        int64_t M, int32_t k, more_gate gate, int32_t* topk_idx,
+                                        float* topk_gate, float* topk_logit, float* lse, float* psum,
+                                        int32_t* counts, float* stats, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  more_status st = validate(0, dt, X, N, h, X, r, X, M, nullptr, k, gate, topk_idx, topk_gate,
+                            topk_logit, lse);
+  if (st != MORE_OK || N == 0) return st;
+  if (!lse || !psum || !counts || !stats) return MORE_ERR_NULL_ARG;
+  if (!aligned16(psum) || !aligned16(counts) || !aligned16(stats)) return MORE_ERR_ALIGNMENT;
+  Layout L;
+  make_layout(0, dt, h, r, M, &L);
+  BalLayout B;
+  if (!balance_layout(dt, L, N, h, M, k, &B)) return MORE_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < B.total || ((uintptr_t)workspace % kAlign) != 0)
+    return MORE_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  hipStream_t hs = (hipStream_t)stream;
+  const bool full = gate == MORE_GATE_FULL_SOFTMAX;
+  LowRankArgs a;
+  memset(&a, 0, sizeof a);
+  a.X = X;
+  a.N = N;
+  a.h = (int)h;
+  a.NT = L.NT;
+  a.k = k;
+  a.R1p = ws + L.off_r1p;
+  a.R2p = ws + L.off_r2p;
+  a.biasp = (const float*)(ws + L.off_bias);
+  a.biasq = (const uint32_t*)(ws + L.off_biasq);
+  a.perm = (const int*)(ws + L.off_perm);
+  a.out_idx = topk_idx;
+  a.out_gate = topk_gate;
+  a.out_logit = topk_logit;
+  a.out_lse = lse;
+  // 1. forward: z to the scratch, top-k + gates + lse (pass 1 over every tile)
+  st = launch_split(a, L, h, kmax_for(k), full, true, ws, hs);
+  if (st != MORE_OK) return st;
+  // 2. second sweep: psum; counts; column sums; L_bal and H_norm
+  const int64_t nb = (N + kTile - 1) / kTile;
+  PsumArgs pa;
+  pa.Z = ws + B.off_z;
+  pa.lse = lse;
+  pa.R2p = a.R2p;
+  pa.biasp = a.biasp;
+  pa.part = (float*)(ws + B.off_part);
+  pa.N = N;
+  pa.NB = (int)nb;
+  pa.NT = L.NT;
+  pa.G = (L.NT + kBalWaves * bal_tiles(L.r16) - 1) / (kBalWaves * bal_tiles(L.r16));
+  pa.slots = B.slots;
+  CountArgs ca;
+  ca.idx = topk_idx;
+  ca.cpart = (int*)(ws + B.off_cpart);
+  ca.N = N;
+  ca.k = k;
+  ca.M = (int)M;
+  ca.NB = (int)nb;
+  ca.slots = B.slots;
+  ColsumArgs sa;
+  sa.part = pa.part;
+  sa.cpart = ca.cpart;
+  sa.perm = a.perm;
+  sa.psum = psum;
+  sa.counts = counts;
+  sa.M = (int)M;
+  sa.Mpad = L.Mpad;
+  sa.slots = B.slots;
+  StatsArgs ta;
+  ta.psum = psum;
+  ta.counts = counts;
+  ta.stats = stats;
+  ta.N = N;
+  ta.k = k;
+  ta.M = (int)M;
+  return launch_balance(L.r16, pa, ca, sa, ta, hs) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 
 more_status more_route_fullrank(more_dtype dt, const void* X, int64_t N, int64_t h, const void* W,

@@ -277,7 +277,7 @@ struct RouteLds {
   static constexpr size_t bytes(int waves, long long mpad) { return flag_off(waves, mpad) + 16; }
 };
 
-template <int KMAX, bool FULL, int R16, int WAVES>
+template <int KMAX, bool FULL, int R16, int WAVES, bool LSE>
 __global__ __launch_bounds__(64 * WAVES) void route_kernel(RouteArgs ra) {
   typedef RouteLds<KMAX> L;
   constexpr int CAPG = L::CAPG;
@@ -320,9 +320,9 @@ __global__ __launch_bounds__(64 * WAVES) void route_kernel(RouteArgs ra) {
   const float* lb = (const float*)(rt_lds + L::bias_off(WAVES));
   lds_cu16* perm = (lds_cu16*)(rt_lds + L::perm_off(WAVES, mpad));
   const rsrc_t r2d = make_rsrc(a.R2p, NT * R16 * 1024);
-  // seed-pass length: the full-softmax gate needs pass 1 over every tile, and
-  // without a bias the sweep order carries no hint (plain two passes)
-  const int P = (FULL || !has_bias) ? NT : ra.pre;
+  // seed-pass length: the full-softmax normaliser needs pass 1 over every
+  // tile, and without a bias the sweep order carries no hint (plain two passes)
+  const int P = (LSE || !has_bias) ? NT : ra.pre;
 
   struct Ops {
     bf16x8 w[R16];
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(64 * WAVES) void route_kernel(RouteArgs ra) {
   for (int jj = 0; jj < nj; ++jj) {
     st.init(a.k);
     sweep(
-        P, [&](const floatx16& acc, int) { tp_pass1_tile<KMAX, FULL>(st, acc); return 0; },
+        P, [&](const floatx16& acc, int) { tp_pass1_tile<KMAX, LSE>(st, acc); return 0; },
         [&](const floatx16&, int, int) {});
     tp_threshold<KMAX>(st, hi, a.k);
     sweep(
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(64 * WAVES) void route_kernel(RouteArgs ra) {
     // z of the next block: requested now, behind the ring's refill, so it has
     // arrived by the time the next seed pass starts
     if (jj + 1 < nj) load_z(jj + 1);
-    tp_finish_groups<KMAX, FULL>(st, lg, lane, hi, perm, a.k, a.out_logit != nullptr, stg);
+    tp_finish_groups<KMAX, FULL, LSE>(st, lg, lane, hi, perm, a.k, a.out_logit != nullptr, stg);
     lds_drain();
     // result block -> memory: one 16-byte store per lane and array (32 k <= 256
     // words); the descriptor range drops the rows past N
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(64 * WAVES) void route_kernel(RouteArgs ra) {
       const u32x4 vl = lds_ld128(sb, S::kLogit * 4 + lane * 16);
       __builtin_amdgcn_raw_buffer_store_b128(vl, make_rsrc(a.out_logit + n0 * a.k, bk), lane * 16, 0, 0);
     }
-    if (FULL && a.out_lse) {
+    if (LSE && a.out_lse) {
       const u32x4 vz = lds_ld128(sb, S::kLse * 4 + lane * 16);
       __builtin_amdgcn_raw_buffer_store_b128(vz, make_rsrc(a.out_lse + n0, (int)rows * 4), lane * 16, 0, 0);
     }

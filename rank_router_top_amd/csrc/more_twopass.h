@@ -300,8 +300,10 @@ __device__ __forceinline__ void tp_pass2_groups(TwoPassState<KMAX>& st, const fl
 // End of a token block (group log): merge the two logs of each token by
 // (logit desc, expert index asc), form the gates and write them to the wave's
 // result block `stg` (LDS).  Logits below both halves' thresholds (lower
-// bounds of the token's k-th) are skipped.  Whole wave active on entry.
-template <int KMAX, bool FULL, class PT>
+// bounds of the token's k-th) are skipped.  LSE: pass 1 accumulated the
+// full-softmax normaliser and lse goes to the result block (FULL implies it).
+// Whole wave active on entry.
+template <int KMAX, bool FULL, bool LSE, class PT>
 __device__ __forceinline__ void tp_finish_groups(const TwoPassState<KMAX>& st, GroupLog lg, int lane, bool hi_half,
                                                  PT perm, int k, bool want_logit, lds_f32* stg);
 
@@ -411,14 +413,15 @@ __device__ __noinline__ void tp_order_groups_slow(GroupLog lg, int lane, int cnt
   }
 }
 
-template <int KMAX, bool FULL, class PT>
+template <int KMAX, bool FULL, bool LSE, class PT>
 __device__ __forceinline__ void tp_finish_groups(const TwoPassState<KMAX>& st, GroupLog lg, int lane, bool hi_half,
                                                  PT perm, int k, bool want_logit, lds_f32* stg) {
+  static_assert(LSE || !FULL, "the full-softmax gate needs the normaliser");
   typedef TpStage<KMAX> S;
   const int cnt_p = (int)partner_u32((uint32_t)st.cnt, hi_half);
   const float thr = fmaxf(st.thr, partner_f32(st.thr, hi_half));
   float lse = 0.f;
-  if (FULL) {
+  if (LSE) {
     // eq. (8) across the two halves of the token
     const float mp = partner_f32(st.m, hi_half), Zp = partner_f32(st.Z, hi_half);
     const float mm = fmaxf(st.m, mp);
@@ -509,7 +512,7 @@ __device__ __forceinline__ void tp_finish_groups(const TwoPassState<KMAX>& st, G
     for (int j = 0; j < KMAX; ++j)
       if (j < k) stg[S::kLogit + o + j] = V[j];
   }
-  if (FULL) stg[S::kLse + lane] = lse;
+  if (LSE) stg[S::kLse + lane] = lse;
 }
 
 }  // namespace more

@@ -17,11 +17,14 @@ LIB_PATH = os.path.join(PKG, "libmore_route.so")
 MORE_DT_BF16, MORE_DT_F32 = 0, 1
 MORE_GATE_TOPK_SOFTMAX, MORE_GATE_FULL_SOFTMAX = 0, 1
 MORE_OK = 0
+MORE_ERR_WORKSPACE = 6
+MORE_ERR_UNSUPPORTED = 7
 STATUS_NAMES = {0: "MORE_OK", 1: "MORE_ERR_NULL_ARG", 2: "MORE_ERR_BAD_SHAPE", 3: "MORE_ERR_BAD_K",
                 4: "MORE_ERR_BAD_DTYPE", 5: "MORE_ERR_BAD_GATE", 6: "MORE_ERR_WORKSPACE",
                 7: "MORE_ERR_UNSUPPORTED", 8: "MORE_ERR_HIP", 9: "MORE_ERR_ALIGNMENT"}
 EXPORTS = ("more_route_lowrank", "more_route_fullrank", "more_route_workspace_bytes",
-           "more_status_str", "more_abi_version", "more_lowrank_pack", "more_lowrank_route_packed")
+           "more_status_str", "more_abi_version", "more_lowrank_pack", "more_lowrank_route_packed",
+           "more_lowrank_balance_packed", "more_balance_workspace_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -54,6 +57,11 @@ def lib() -> C.CDLL:
             L.more_lowrank_route_packed.argtypes = [i32, p, i64, i64, i64, i64, i32, i32,
                                                     p, p, p, p, p, C.c_size_t, p]
             L.more_lowrank_route_packed.restype = C.c_int
+            L.more_lowrank_balance_packed.argtypes = [i32, p, i64, i64, i64, i64, i32, i32,
+                                                      p, p, p, p, p, p, p, p, C.c_size_t, p]
+            L.more_lowrank_balance_packed.restype = C.c_int
+            L.more_balance_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i32]
+            L.more_balance_workspace_bytes.restype = C.c_size_t
             L.more_route_workspace_bytes.argtypes = [C.c_int, i32, i64, i64, i64, i64, i32, i32, C.c_int]
             L.more_route_workspace_bytes.restype = C.c_size_t
             L.more_status_str.argtypes = [C.c_int]
@@ -151,6 +159,30 @@ def route_lowrank_packed(X, r: int, M: int, k: int, gate: int, workspace, *, out
     _check("more_lowrank_route_packed", lib().more_lowrank_route_packed(
         dt, _ptr(X), N, h, r, M, k, gate, _ptr(o["idx"]), _ptr(o["gate"]), _ptr(o.get("logit")),
         _ptr(o.get("lse")), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return o
+
+
+def balance_workspace_bytes(dt: int, N: int, h: int, r: int, M: int, k: int) -> int:
+    return int(lib().more_balance_workspace_bytes(dt, N, h, r, M, k))
+
+
+def balance_lowrank_packed(X, r: int, M: int, k: int, gate: int, workspace, *, out=None,
+                           want_logit: bool = True, stream=None) -> dict:
+    """more_lowrank_balance_packed: the routing results plus lse, psum (M),
+    counts (M) and stats = (L_bal, H_norm), against weights packed by
+    pack_lowrank into `workspace` (sized by balance_workspace_bytes)."""
+    import torch
+    dt = _dtype_code(X)
+    N, h = X.shape
+    o = _outputs(X, k, want_logit, True, out)
+    if "psum" not in o:
+        o["psum"] = torch.empty((M,), dtype=torch.float32, device=X.device)
+        o["counts"] = torch.empty((M,), dtype=torch.int32, device=X.device)
+        o["stats"] = torch.empty((4,), dtype=torch.float32, device=X.device)
+    _check("more_lowrank_balance_packed", lib().more_lowrank_balance_packed(
+        dt, _ptr(X), N, h, r, M, k, gate, _ptr(o["idx"]), _ptr(o["gate"]), _ptr(o.get("logit")),
+        _ptr(o["lse"]), _ptr(o["psum"]), _ptr(o["counts"]), _ptr(o["stats"]), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
     return o
 
 

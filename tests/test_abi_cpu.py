@@ -91,3 +91,44 @@ def test_fullrank_rejects_bad_arguments():
     assert f(0, FAKE, 64, 63, FAKE, 32, None, 4, 0, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == 7
     assert f(0, None, 64, 64, FAKE, 32, None, 4, 0, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == 1
     assert f(0, FAKE, 64, 64, FAKE, 32, None, 4, 0, FAKE, FAKE, None, None, FAKE, 16, None) == 6
+
+
+def call_balance(dt=0, N=64, h=256, r=32, M=4096, k=8, gate=0, idx=FAKE, g=FAKE, logit=None, lse=FAKE,
+                 psum=FAKE, counts=FAKE, stats=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return R.lib().more_lowrank_balance_packed(dt, FAKE, N, h, r, M, k, gate, idx, g, logit, lse, psum,
+                                               counts, stats, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=16), 7), (dict(r=128), 7), (dict(dt=1), 7), (dict(M=6000), 7), (dict(M=14721, k=4), 7), (dict(M=14720, k=4, ws_bytes=100), 6),
+    (dict(lse=None), 1), (dict(psum=None), 1), (dict(counts=None), 1), (dict(stats=None), 1),
+    (dict(psum=ODD), 9), (dict(ws_bytes=100), 6), (dict(gate=2), 5), (dict(k=0), 3), (dict(h=60), 7),
+])
+def test_balance_rejects_bad_arguments_before_any_hip_call(kw, code):
+    assert call_balance(**kw) == code
+
+
+def test_balance_empty_batch_is_a_noop():
+    assert call_balance(N=0, idx=None, g=None, lse=None, psum=None, counts=None, stats=None) == 0
+
+
+def test_balance_workspace_bytes():
+    """Packed weights + z scratch (4 bytes per token and rank) + per-slot
+    partial sums: fp32 by sweep position and int32 by expert, one row per
+    token slot (at most 256 slots, one per 32-token block below that)."""
+    bf = R.MORE_DT_BF16
+    route = R.workspace_bytes(False, bf, 262144, 2048, 32, 4096, 8, 0, True)
+    assert R.balance_workspace_bytes(bf, 262144, 2048, 32, 4096, 8) == route + 2 * 256 * 4096 * 4
+    route33 = R.workspace_bytes(False, bf, 33, 2048, 32, 4096, 8, 0, True)
+    assert R.balance_workspace_bytes(bf, 33, 2048, 32, 4096, 8) == route33 + 2 * 2 * 4096 * 4
+    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 5888, 8) > 0
+    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 5889, 8) == 0     # routing LDS of the k <= 8 kernel
+    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 14720, 4) > 0
+    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 14721, 4) == 0
+    assert R.balance_workspace_bytes(R.MORE_DT_F32, 10, 2048, 32, 4096, 8) == 0
+    assert R.balance_workspace_bytes(bf, 10, 2048, 128, 4096, 8) == 0
+    assert R.balance_workspace_bytes(bf, 10, 4608, 16, 4096, 8) > 0       # R1 resident in LDS
+    assert R.balance_workspace_bytes(bf, 10, 4864, 16, 4096, 8) == 0
+    assert R.balance_workspace_bytes(bf, 10, 768, 64, 4096, 8) > 0
+    assert R.balance_workspace_bytes(bf, 10, 1024, 64, 4096, 8) == 0
+    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 4096, 9) == 0

@@ -313,3 +313,33 @@ def test_ties_many_experts(oracle_lib):
         sep = np.all((np.abs(np.diff(lo, axis=1)) == 0) | (np.abs(np.diff(lo, axis=1)) > 1e-3), axis=1)
         sep &= gap_clear(o)
         assert np.array_equal(g["idx"][sep], o["idx"][sep]), "tie rule violated"
+
+
+@pytest.mark.parametrize("gate", [CF.GATE_TOPK_SOFTMAX, CF.GATE_FULL_SOFTMAX])
+def test_headline_full_size(oracle_lib, gate):
+    """Headline workload at full size (N = 262144, h = 2048, M = 4096, r = 32,
+    k = 8, bias) in the launch configuration the benchmark times: weights
+    packed once, workspace for all N tokens (projection + routing kernels).
+    The batch is 32 copies of one 8192-row block of the seeded tokens: the
+    oracle checks the block, and every copy of a row must give bitwise the same
+    indices, gates and logits (rows are routed independently)."""
+    cfg = CF.HEADLINE
+    base_n, reps = 8192, cfg.N // 8192
+    Xb = cfg.x_rows(0, 0, base_n, n_total=cfg.N)
+    R1, R2, b = cfg.weights(0)
+    say(f"full size gate={gate}: oracle on the base block")
+    o = oracle_lib.route_lowrank(Xb, R1, R2, b, cfg.k, gate)
+    say(f"full size gate={gate}: GPU on the tiled batch")
+    X = R.to_device(np.tile(Xb, (reps, 1)), DEV)
+    d = [R.to_device(a, DEV) for a in (R1, R2, b)]
+    nbytes = R.workspace_bytes(False, R.MORE_DT_BF16, cfg.N, cfg.h, cfg.r, cfg.M, cfg.k, gate, True)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    R.pack_lowrank(*d, ws)
+    g = to_np(R.route_lowrank_packed(X, cfg.r, cfg.M, cfg.k, gate, ws))
+    torch.cuda.synchronize()
+    for key in ("idx", "gate", "logit") + (("lse",) if gate else ()):
+        v = g[key].reshape((reps, base_n) + g[key].shape[1:])
+        assert all(np.array_equal(v[c], v[0]) for c in range(1, reps)), key
+    first = {key: (None if v is None else v[:base_n]) for key, v in g.items()}
+    res = compare(o, first, cfg.k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, "full-size")
+    say(f"full size gate={gate}: ok {res}")
