@@ -17,6 +17,10 @@ resident in HBM.  Prints ONE JSON line:
   cpu_baseline   the fp64 oracle on a bounded sample of the same tokens, timed
                  on the host cores (rank 0, one GPU only)
   fullrank       the fused full-rank (standard) router on the same tokens
+  balance        the training forward with balancing statistics
+                 (more_lowrank_balance_packed: routing with the full-softmax
+                 normaliser, then the second sweep for psum, the dispatch
+                 counts, L_bal and H_norm) on the same tokens, HIP-event timed
   context        published B200 figures of the paper (other hardware)
 Only one GPU is supported: --gpus above 1 exits with a message.
 """
@@ -36,6 +40,12 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 ROUTER_KERNELS = ("more::proj_kernel<2, 8, false, 4>", "more::route_kernel<8, false, 2, 8>")
 KERNEL_NAME = " + ".join(ROUTER_KERNELS)
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published (no sparsity)
+# v_exp_f32 rate: 256 CUs x 4 SIMDs x 16 lanes per cycle at half rate (one wave64
+# exp per 8 cycles, measured against v_fma_f32 at one per 4), 2.4 GHz
+EXP_PEAK_PER_S = 256 * 4 * 16 / 2 * 2.4e9
+BALANCE_KERNELS = ("more::proj_kernel<2, 8, false, 4>", "more::route_kernel<8, false, 2, 8, true>",
+                   "more::psum_kernel<2, 8, 8>", "more::count_kernel", "more::colsum_kernel",
+                   "more::stats_kernel")
 CONTEXT = {
     "source": "MoRE: Scaling mixture of experts with hardware-aware low-rank routing (B200, bf16)",
     "note": "other hardware and other shapes; no figure is published at this workload",
@@ -60,6 +70,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fullrank", action="store_true")
+    ap.add_argument("--no-balance", action="store_true")
     ap.add_argument("--fullrank-steps", type=int, default=3)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, "
@@ -281,6 +292,33 @@ def main():
                      "pack_kernel_ms": p_mean},
         "context": CONTEXT,
     }
+
+    nbb = 0 if args.no_balance else R.balance_workspace_bytes(dt, cfg.N, cfg.h, cfg.r, cfg.M, cfg.k)
+    if nbb > 0:
+        wsb = torch.empty(nbb, dtype=torch.uint8, device=dev)
+        R.pack_lowrank(R1, R2, b, wsb, stream=stream)
+        bout = dict(out, lse=torch.empty((cfg.N,), dtype=torch.float32, device=dev),
+                    psum=torch.empty((cfg.M,), dtype=torch.float32, device=dev),
+                    counts=torch.empty((cfg.M,), dtype=torch.int32, device=dev),
+                    stats=torch.empty((4,), dtype=torch.float32, device=dev))
+
+        def balance_call():
+            R.balance_lowrank_packed(X, cfg.r, cfg.M, cfg.k, gate, wsb, out=bout, stream=stream)
+
+        for _ in range(3):
+            balance_call()
+        b_mean, b_med, b_p10, b_p90 = time_events(torch, balance_call, max(args.steps, 20), stream)
+        st = bout["stats"].cpu().tolist()
+        log(f"balance call mean {b_mean:.4f} ms (p10 {b_p10:.4f}, p90 {b_p90:.4f}); "
+            f"L_bal {st[0]:.6f} H_norm {st[1]:.6f}")
+        result["balance"] = {
+            "entry": "more_lowrank_balance_packed", "value": cfg.N / (b_mean * 1e-3), "unit": "tokens/s",
+            "ms_per_call": b_mean, "ms_median": b_med, "ms_p10": b_p10, "ms_p90": b_p90,
+            "extra_ms_over_routing_call": b_mean - k_mean, "kernels": list(BALANCE_KERNELS),
+            "L_bal": st[0], "H_norm": st[1],
+            "exp_count_per_call": 2 * cfg.N * cfg.M,
+            "exp_bound_ms_per_call": 2 * cfg.N * cfg.M / EXP_PEAK_PER_S * 1e3}
+        del wsb, bout
 
     if not args.no_fullrank:
         FR = CF.FULLRANK

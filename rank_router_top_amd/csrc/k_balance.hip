@@ -33,21 +33,40 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(CountArgs a) {
 }
 
 
-// Grid: ceil(Mpad / 256) workgroups of 256 threads, one column each.
+// Grid: ceil(Mpad / 32) workgroups of 256 threads.  Workgroup b owns columns
+// 32b .. 32b + 31; thread (c, q) = (tid % 32, tid / 32) sums slots q, q + 8, ...
+// of column 32b + c, and the eight partial sums are added in order q = 0..7,
+// so the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void colsum_kernel(ColsumArgs a) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= a.Mpad) return;
+  __shared__ float fp[8][32];
+  __shared__ int cp[8][32];
+  const int c = threadIdx.x & 31, q = threadIdx.x >> 5;
+  const int p = blockIdx.x * 32 + c;
   float sp = 0.f;
-  for (int s = 0; s < a.slots; ++s) sp += a.part[(size_t)s * a.Mpad + p];
-  const int ex = a.perm[p];
-  if (ex >= 0 && ex < a.M) a.psum[ex] = sp;
-  if (p < a.M) {
-    int c = 0;
-    for (int s = 0; s < a.slots; ++s) c += a.cpart[(size_t)s * a.M + p];
-    a.counts[p] = c;
+  int sc = 0;
+  if (p < a.Mpad) {
+#pragma unroll 8
+    for (int s = q; s < a.slots; s += 8) sp += a.part[(size_t)s * a.Mpad + p];
   }
+  if (p < a.M) {
+#pragma unroll 8
+    for (int s = q; s < a.slots; s += 8) sc += a.cpart[(size_t)s * a.M + p];
+  }
+  fp[q][c] = sp;
+  cp[q][c] = sc;
+  __syncthreads();
+  if (q != 0 || p >= a.Mpad) return;
+  float tp = 0.f;
+  int tc = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    tp += fp[i][c];
+    tc += cp[i][c];
+  }
+  const int ex = a.perm[p];
+  if (ex >= 0 && ex < a.M) a.psum[ex] = tp;
+  if (p < a.M) a.counts[p] = tc;
 }
-
 
 // One workgroup of 1024 threads.  With c_i the counts and C = N k:
 //   L_bal = M sum_i (c_i / C) (psum_i / N)
@@ -97,7 +116,7 @@ hipError_t launch_balance(int r16, const PsumArgs& pa, const CountArgs& ca, cons
   const int E = (ca.M + kCountBins - 1) / kCountBins;
   hipLaunchKernelGGL(count_kernel, dim3((unsigned)(ca.slots * E)), dim3(kCountThreads), 0, stream, ca);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((sa.Mpad + 255) / 256)), dim3(256), 0, stream, sa);
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((sa.Mpad + 31) / 32)), dim3(256), 0, stream, sa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(1024), 0, stream, ta);
   return hipGetLastError();

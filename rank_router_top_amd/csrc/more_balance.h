@@ -76,13 +76,13 @@ __global__ __launch_bounds__(64 * WAVES) void psum_kernel(PsumArgs a) {
   float cs[TW];
 #pragma unroll
   for (int u = 0; u < TW; ++u) cs[u] = 0.f;
-  // operands of one token block: z (bf16 hi, lo) and the accumulator start,
-  // -lse of token 8q + 4hf + e (register 4q + e); tokens past N start at -inf
-  // and contribute exp2(-inf) = 0.  The next block's are requested before the
-  // current one is swept.
+  // operands of one token block: z (bf16 hi, lo) and lse of token
+  // 8q + 4hf + e of the block (register 4q + e).  Two buffers in turn: the
+  // next block's loads are issued before the current block is swept, and
+  // nothing reads them until its own sweep (no early wait on the queue).
   struct Blk {
     bf16x8 zh[R16], zl[R16];
-    floatx16 c0;
+    float lr[16];
   };
   auto load_blk = [&](long long j, Blk& b) {
     const rsrc_t zd = make_rsrc((const char*)a.Z + (size_t)j * z_block_bytes(R16), z_block_bytes(R16));
@@ -95,21 +95,25 @@ __global__ __launch_bounds__(64 * WAVES) void psum_kernel(PsumArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const long long tok = n0 + 8 * (v >> 2) + (v & 3);
-      b.c0[v] = tok < a.N ? -a.lse[tok] : -__builtin_inff();
+      b.lr[v] = a.lse[tok < a.N ? tok : a.N - 1];   // clamped: the row is dropped below
     }
   };
-  Blk cur, nxt;
-  long long j = s;
-  if (j < a.NB) load_blk(j, cur);
-  for (; j < a.NB; j += a.slots) {
-    if (j + a.slots < a.NB) load_blk(j + a.slots, nxt);
+  auto sweep_blk = [&](long long j, const Blk& b) {
+    // the block's operands are first touched here, after the loads of the
+    // other buffer have been issued (the scheduler may not hoist the uses)
+    __builtin_amdgcn_sched_barrier(0);
+    // accumulator start -lse; tokens past N start at -inf and add exp2(-inf) = 0
+    floatx16 c0;
+    const long long n0 = j * kTile + 4 * hf;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) c0[v] = n0 + 8 * (v >> 2) + (v & 3) < a.N ? -b.lr[v] : -__builtin_inff();
 #pragma unroll
     for (int u = 0; u < TW; ++u) {
-      floatx16 acc = cur.c0;
+      floatx16 acc = c0;
 #pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(cur.zh[m], w[u][m], acc);
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(b.zh[m], w[u][m], acc);
 #pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(cur.zl[m], w[u][m], acc);
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(b.zl[m], w[u][m], acc);
       float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; v += 4) {
@@ -120,7 +124,20 @@ __global__ __launch_bounds__(64 * WAVES) void psum_kernel(PsumArgs a) {
       }
       cs[u] += (p0 + p1) + (p2 + p3);
     }
-    cur = nxt;
+  };
+  // Loads are issued unconditionally (past the last block they re-read the
+  // last one and are never swept), so the wait counts stay static.
+  Blk b0, b1;
+  const long long st = a.slots, last = a.NB - 1;
+  long long j = s;
+  load_blk(j, b0);   // s < slots <= NB
+  for (;; j += 2 * st) {
+    load_blk(j + st < last ? j + st : last, b1);
+    sweep_blk(j, b0);
+    if (j + st >= a.NB) break;
+    load_blk(j + 2 * st < last ? j + 2 * st : last, b0);
+    sweep_blk(j + st, b1);
+    if (j + 2 * st >= a.NB) break;
   }
   // both halves of a lane pair hold the same expert: add them, the low half stores
   float* row = a.part + (size_t)s * mpad;

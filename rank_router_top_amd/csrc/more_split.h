@@ -320,9 +320,10 @@ __global__ __launch_bounds__(64 * WAVES) void route_kernel(RouteArgs ra) {
   const float* lb = (const float*)(rt_lds + L::bias_off(WAVES));
   lds_cu16* perm = (lds_cu16*)(rt_lds + L::perm_off(WAVES, mpad));
   const rsrc_t r2d = make_rsrc(a.R2p, NT * R16 * 1024);
-  // seed-pass length: the full-softmax normaliser needs pass 1 over every
-  // tile, and without a bias the sweep order carries no hint (plain two passes)
-  const int P = (LSE || !has_bias) ? NT : ra.pre;
+  // seed-pass length: without a bias the sweep order carries no hint (plain
+  // two passes).  The full-softmax normaliser is accumulated in pass 2, which
+  // covers every tile.
+  const int P = has_bias ? ra.pre : NT;
 
   struct Ops {
     bf16x8 w[R16];
@@ -402,11 +403,16 @@ __global__ __launch_bounds__(64 * WAVES) void route_kernel(RouteArgs ra) {
   for (int jj = 0; jj < nj; ++jj) {
     st.init(a.k);
     sweep(
-        P, [&](const floatx16& acc, int) { tp_pass1_tile<KMAX, LSE>(st, acc); return 0; },
+        P, [&](const floatx16& acc, int) { tp_pass1_tile<KMAX, false>(st, acc); return 0; },
         [&](const floatx16&, int, int) {});
     tp_threshold<KMAX>(st, hi, a.k);
     sweep(
-        NT, [&](const floatx16& acc, int) { return tp_pass2_scan<KMAX, false>(st, acc, false); },
+        NT,
+        [&](const floatx16& acc, int) {
+          const floatx4 g = tp_pass2_scan<KMAX, false>(st, acc, false);
+          if (LSE) tp_lse_tile<KMAX>(st, acc, g);
+          return g;
+        },
         [&](const floatx16& acc, int t, const floatx4& g) {
           tp_pass2_groups<KMAX, CAPG>(st, acc, g, kTile * t + 4 * hf, lg, lane, perm, a.k);
         });

@@ -145,6 +145,23 @@ __device__ __forceinline__ floatx4 tp_pass2_scan(TwoPassState<KMAX>& st, const f
   return g;
 }
 
+// eq. (8) over one pass-2 tile (group maxima g from tp_pass2_scan): rescale
+// the running sum when the maximum moves, then add the tile.
+template <int KMAX>
+__device__ __forceinline__ void tp_lse_tile(TwoPassState<KMAX>& st, const floatx16& acc, const floatx4& g) {
+  const float tmax = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
+  const float mn = fmaxf(st.m, tmax);
+  const float mb = mn * kLog2e;
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; v += 2) {
+    s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kLog2e, -mb));
+    s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v + 1], kLog2e, -mb));
+  }
+  st.Z = st.Z * __builtin_amdgcn_exp2f((st.m - mn) * kLog2e) + (s0 + s1);
+  st.m = mn;
+}
+
 // The appends of a pass-2 tile (group maxima g from tp_pass2_scan).
 template <int KMAX, int CAP, class PT>
 __device__ __forceinline__ void tp_pass2_log(TwoPassState<KMAX>& st, const floatx16& acc, const floatx4& g,
