@@ -189,5 +189,21 @@ def balance_lowrank(X, R1, R2, bias, k: int, gate: int = GATE_TOPK, nthreads: in
     return out
 
 
+def dispatch_sort(idx, M: int) -> dict:
+    """Expert dispatch after the router (App. E, Fig. 9: "sort + count",
+    (N, k) -> N k sorted indices + offsets).  The N k selected slots, numbered
+    s = n k + j in row-major order of idx, are ordered by expert, slots of the
+    same expert in increasing s (a stable sort: a library sort is the step);
+    offsets[e] is where expert e's run starts, offsets[M] = N k."""
+    keys = np.ascontiguousarray(idx).astype(np.int64).reshape(-1)
+    if keys.size and (keys.min() < 0 or keys.max() >= M):
+        raise ValueError("expert index outside [0, M)")
+    order = np.argsort(keys, kind="stable")
+    offsets = np.zeros(M + 1, np.int64)
+    offsets[1:] = np.cumsum(np.bincount(keys, minlength=M))
+    return dict(sorted_expert=keys[order].astype(np.int32), sorted_slot=order.astype(np.int32),
+                offsets=offsets.astype(np.int32))
+
+
 def max_threads() -> int:
     return int(_load().oracle_max_threads())

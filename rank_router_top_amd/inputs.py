@@ -114,3 +114,36 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == DT_BF16:
         return bf16_bits_to_f32(a).astype(np.float64)
     return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+TENSOR_SETS = 5
+
+
+def make_expert_sets(seed: int, cfg_id: int, N: int, M: int, k: int, skew: float = 0.7) -> np.ndarray:
+    """N x k int32 rows of k distinct experts in [0, M), in drawn order: the
+    shape of a router's selected indices.  Experts are drawn from a skewed
+    categorical distribution, p_e proportional to exp(skew * g_e) with
+    g_e ~ N(0, 1) (a biased router concentrates load the same way), and rows
+    that drew an expert twice are drawn again until every row is distinct."""
+    if not (1 <= k <= M):
+        raise ValueError("need 1 <= k <= M")
+    rng = _rng(seed, cfg_id, TENSOR_SETS)
+    p = np.exp(skew * rng.standard_normal(M))
+    cdf = np.cumsum(p / p.sum())
+    cdf[-1] = 1.0
+
+    def draw(n):
+        return np.minimum(np.searchsorted(cdf, rng.random((n, k)), side="right"), M - 1).astype(np.int32)
+
+    out = draw(N)
+    while True:
+        s = np.sort(out, axis=1)
+        bad = np.nonzero(np.any(s[:, 1:] == s[:, :-1], axis=1))[0] if k > 1 else np.zeros(0, np.int64)
+        if bad.size == 0:
+            return out
+        if k > M // 2:
+            # dense rows: a uniformly random k-subset per offending row
+            for i in bad:
+                out[i] = rng.permutation(M)[:k]
+        else:
+            out[bad] = draw(bad.size)
