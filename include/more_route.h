@@ -178,6 +178,32 @@ more_status more_lowrank_balance_packed(more_dtype dt, const void* X, int64_t N,
 size_t more_balance_workspace_bytes(more_dtype dt, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k);
 
 /*
+ * Expert dispatch after the router (App. E, Fig. 9: "sort + count", the
+ * (N, k) selected indices become N k indices sorted by expert + offsets).
+ *   topk_idx       N x k int32 expert indices, each in [0, M) (the router's
+ *                  topk_idx).  Entries outside [0, M) give an unspecified
+ *                  order but no access outside the outputs.
+ *   sorted_expert  N k int32: the experts in non-decreasing order.
+ *   sorted_slot    N k int32: slot s = n k + j of each entry (token n = s / k,
+ *                  its j-th choice); within one expert the slots increase
+ *                  (stable), so the result is unique.
+ *   offsets        M + 1 int32: expert e owns positions offsets[e] ..
+ *                  offsets[e+1] - 1; offsets[M] = N k.
+ *   workspace      at least more_dispatch_workspace_bytes(N, k, M) bytes,
+ *                  256-byte aligned (per-block digit counts; for M > 64 one
+ *                  extra N k key + slot buffer), overwritten.
+ * Contract: N k < 2^31 - 1, 1 <= k <= M <= 2^24.  N = 0 is a no-op.  Integer
+ * work only: the result is exact and deterministic.
+ */
+more_status more_dispatch_sort(const int32_t* topk_idx, int64_t N, int32_t k, int64_t M, int32_t* sorted_expert,
+                               int32_t* sorted_slot, int32_t* offsets, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Workspace bytes of more_dispatch_sort (0 for arguments it rejects).  Pure
+ * host function, no HIP call. */
+size_t more_dispatch_workspace_bytes(int64_t N, int32_t k, int64_t M);
+
+/*
  * Fused standard (full-rank) router + top-k + gates: the same selection and
  * gates with l = x W + b (§2 standard router; App. H.3 Fig. 20 fuses it the
  * same way, reloading weight tiles instead of a rank-r intermediate).

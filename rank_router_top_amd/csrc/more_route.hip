@@ -20,6 +20,7 @@
 #include "more_pack.h"
 #include "more_dispatch.h"
 #include "more_balance.h"
+#include "more_sort.h"
 
 using namespace more;
 
@@ -547,6 +548,43 @@ more_status more_lowrank_balance_packed(more_dtype dt, const void* X, int64_t N,
   ta.k = k;
   ta.M = (int)M;
   return launch_balance(L.r16, pa, ca, sa, ta, hs) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+}
+
+size_t more_dispatch_workspace_bytes(int64_t N, int32_t k, int64_t M) {
+  if (N < 0 || k < 1 || M < 1 || M > (1 << 24) || (int64_t)k > M || N * (int64_t)k >= ((int64_t)1 << 31) - 1)
+    return 0;
+  const int64_t n = N * k;
+  const int64_t B = (n + kSortBlock - 1) / kSortBlock;
+  size_t bytes = align_up((size_t)(B > 0 ? B : 1) * kSortBuckets * sizeof(int));
+  if (sort_passes(M) > 1) bytes += 2 * align_up((size_t)(n > 0 ? n : 1) * sizeof(int));
+  return bytes;
+}
+
+more_status more_dispatch_sort(const int32_t* topk_idx, int64_t N, int32_t k, int64_t M, int32_t* sorted_expert,
+                               int32_t* sorted_slot, int32_t* offsets, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (N < 0 || M < 1 || M > (1 << 24)) return MORE_ERR_BAD_SHAPE;
+  if (k < 1 || (int64_t)k > M) return MORE_ERR_BAD_K;
+  if (N * (int64_t)k >= ((int64_t)1 << 31) - 1) return MORE_ERR_BAD_SHAPE;
+  if (N == 0) return MORE_OK;
+  if (!topk_idx || !sorted_expert || !sorted_slot || !offsets) return MORE_ERR_NULL_ARG;
+  if (!aligned16(topk_idx) || !aligned16(sorted_expert) || !aligned16(sorted_slot) || !aligned16(offsets))
+    return MORE_ERR_ALIGNMENT;
+  const size_t need = more_dispatch_workspace_bytes(N, k, M);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0) return MORE_ERR_WORKSPACE;
+  const int n = (int)(N * k);
+  const int64_t B = (n + kSortBlock - 1) / kSortBlock;
+  char* ws = (char*)workspace;
+  int* hist = (int*)ws;
+  int* tk = nullptr;
+  int* tv = nullptr;
+  if (sort_passes(M) > 1) {
+    const size_t off = align_up((size_t)B * kSortBuckets * sizeof(int));
+    tk = (int*)(ws + off);
+    tv = (int*)(ws + off + align_up((size_t)n * sizeof(int)));
+  }
+  return launch_dispatch_sort(topk_idx, n, (int)M, sorted_expert, sorted_slot, offsets, hist, tk, tv,
+                              (hipStream_t)stream) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 
 more_status more_route_fullrank(more_dtype dt, const void* X, int64_t N, int64_t h, const void* W,

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "MORE_OK", 1: "MORE_ERR_NULL_ARG", 2: "MORE_ERR_BAD_SHAPE", 3
                 7: "MORE_ERR_UNSUPPORTED", 8: "MORE_ERR_HIP", 9: "MORE_ERR_ALIGNMENT"}
 EXPORTS = ("more_route_lowrank", "more_route_fullrank", "more_route_workspace_bytes",
            "more_status_str", "more_abi_version", "more_lowrank_pack", "more_lowrank_route_packed",
-           "more_lowrank_balance_packed", "more_balance_workspace_bytes")
+           "more_lowrank_balance_packed", "more_balance_workspace_bytes", "more_dispatch_sort",
+           "more_dispatch_workspace_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -61,6 +62,10 @@ def lib() -> C.CDLL:
                                                       p, p, p, p, p, p, p, p, C.c_size_t, p]
             L.more_lowrank_balance_packed.restype = C.c_int
             L.more_balance_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i32]
+            L.more_dispatch_sort.argtypes = [p, i64, i32, i64, p, p, p, p, C.c_size_t, p]
+            L.more_dispatch_sort.restype = C.c_int
+            L.more_dispatch_workspace_bytes.argtypes = [i64, i32, i64]
+            L.more_dispatch_workspace_bytes.restype = C.c_size_t
             L.more_balance_workspace_bytes.restype = C.c_size_t
             L.more_route_workspace_bytes.argtypes = [C.c_int, i32, i64, i64, i64, i64, i32, i32, C.c_int]
             L.more_route_workspace_bytes.restype = C.c_size_t
@@ -184,6 +189,26 @@ def balance_lowrank_packed(X, r: int, M: int, k: int, gate: int, workspace, *, o
         _ptr(o["lse"]), _ptr(o["psum"]), _ptr(o["counts"]), _ptr(o["stats"]), _ptr(workspace),
         workspace.numel(), _stream(stream)))
     return o
+
+
+def dispatch_workspace_bytes(N: int, k: int, M: int) -> int:
+    return int(lib().more_dispatch_workspace_bytes(N, k, M))
+
+
+def dispatch_sort(idx, M: int, *, out=None, workspace=None, stream=None) -> dict:
+    """more_dispatch_sort on an N x k int32 device tensor: returns
+    dict(sorted_expert, sorted_slot, offsets)."""
+    import torch
+    N, k = idx.shape
+    if out is None:
+        out = dict(sorted_expert=torch.empty((N * k,), dtype=torch.int32, device=idx.device),
+                   sorted_slot=torch.empty((N * k,), dtype=torch.int32, device=idx.device),
+                   offsets=torch.empty((M + 1,), dtype=torch.int32, device=idx.device))
+    ws = _workspace(dispatch_workspace_bytes(N, k, M), workspace, idx.device)
+    _check("more_dispatch_sort", lib().more_dispatch_sort(
+        _ptr(idx), N, k, M, _ptr(out["sorted_expert"]), _ptr(out["sorted_slot"]), _ptr(out["offsets"]),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
 
 
 def route_fullrank(X, W, bias, k: int, gate: int = MORE_GATE_TOPK_SOFTMAX, *, out=None,

@@ -132,3 +132,19 @@ def test_balance_workspace_bytes():
     assert R.balance_workspace_bytes(bf, 10, 768, 64, 4096, 8) > 0
     assert R.balance_workspace_bytes(bf, 10, 1024, 64, 4096, 8) == 0
     assert R.balance_workspace_bytes(bf, 10, 2048, 32, 4096, 9) == 0
+
+
+def test_dispatch_workspace_and_validation():
+    """Digit counts (64 per block of 8192 entries, 256-byte aligned) and, for
+    more than one radix pass (M > 64), a key and a slot buffer of N k entries."""
+    assert R.dispatch_workspace_bytes(262144, 8, 4096) == 256 * 64 * 4 + 2 * 262144 * 8 * 4
+    assert R.dispatch_workspace_bytes(1000, 4, 64) == 256
+    assert R.dispatch_workspace_bytes(1000, 5, 4) == 0          # k > M
+    assert R.dispatch_workspace_bytes(1 << 28, 8, 4096) == 0     # N k >= 2^31 - 1
+    f = R.lib().more_dispatch_sort
+    assert f(FAKE, 10, 4, 2, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 3      # k > M
+    assert f(None, 10, 4, 64, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert f(ODD, 10, 4, 64, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 9
+    assert f(FAKE, 10, 4, 64, FAKE, FAKE, FAKE, FAKE, 16, None) == 6
+    assert f(FAKE, 0, 4, 64, None, None, None, None, 0, None) == 0            # N = 0: no-op
+    assert f(FAKE, -1, 4, 64, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 2
