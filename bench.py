@@ -21,6 +21,10 @@ resident in HBM.  Prints ONE JSON line:
                  (more_lowrank_balance_packed: routing with the full-softmax
                  normaliser, then the second sweep for psum, the dispatch
                  counts, L_bal and H_norm) on the same tokens, HIP-event timed
+  dispatch       the expert dispatch (more_dispatch_sort: the N x k indices
+                 the routing call returned -> expert-sorted slots + offsets),
+                 HIP-event timed, algorithmic bytes (read N k indices, write
+                 N k experts + N k slots + M + 1 offsets) against 8 TB/s
   context        published B200 figures of the paper (other hardware)
 Only one GPU is supported: --gpus above 1 exits with a message.
 """
@@ -71,6 +75,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fullrank", action="store_true")
     ap.add_argument("--no-balance", action="store_true")
+    ap.add_argument("--no-dispatch", action="store_true")
     ap.add_argument("--fullrank-steps", type=int, default=3)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, "
@@ -319,6 +324,30 @@ def main():
             "exp_count_per_call": 2 * cfg.N * cfg.M,
             "exp_bound_ms_per_call": 2 * cfg.N * cfg.M / EXP_PEAK_PER_S * 1e3}
         del wsb, bout
+
+    if not args.no_dispatch:
+        nk = cfg.N * cfg.k
+        dws = torch.empty(max(R.dispatch_workspace_bytes(cfg.N, cfg.k, cfg.M), 1), dtype=torch.uint8, device=dev)
+        dout = dict(sorted_expert=torch.empty((nk,), dtype=torch.int32, device=dev),
+                    sorted_slot=torch.empty((nk,), dtype=torch.int32, device=dev),
+                    offsets=torch.empty((cfg.M + 1,), dtype=torch.int32, device=dev))
+        kernel_only()   # the routing call's own indices
+
+        def dispatch_call():
+            R.dispatch_sort(out["idx"], cfg.M, out=dout, workspace=dws, stream=stream)
+
+        for _ in range(3):
+            dispatch_call()
+        d_mean, d_med, d_p10, d_p90 = time_events(torch, dispatch_call, max(args.steps, 20), stream)
+        d_bytes = nk * 4 + 2 * nk * 4 + (cfg.M + 1) * 4
+        d_ach = d_bytes / (d_mean * 1e-3) / 1e9
+        log(f"dispatch call mean {d_mean:.4f} ms (p10 {d_p10:.4f}, p90 {d_p90:.4f})")
+        result["dispatch"] = {
+            "entry": "more_dispatch_sort", "ms_per_call": d_mean, "ms_median": d_med, "ms_p10": d_p10,
+            "ms_p90": d_p90, "entries": nk, "radix_passes": 2 if cfg.M > 64 else 1,
+            "roofline": {"bound": "hbm", "achieved": d_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": d_ach / HBM_PEAK_GBS, "algorithmic_bytes_per_call": d_bytes}}
+        del dws, dout
 
     if not args.no_fullrank:
         FR = CF.FULLRANK

@@ -7,41 +7,94 @@ namespace more {
 
 __device__ __forceinline__ int sort_digit(int key, int shift) { return (int)(((unsigned)key >> shift) & (kSortBuckets - 1)); }
 
+// Lanes of the wave holding digit d (among the lanes where ok is set).
+__device__ __forceinline__ unsigned long long sort_peers(int d, bool ok) {
+  unsigned long long peers = __builtin_amdgcn_ballot_w64(ok);
+#pragma unroll
+  for (int bit = 0; bit < kSortDigitBits; ++bit) {
+    const unsigned long long b = __builtin_amdgcn_ballot_w64(((d >> bit) & 1) != 0);
+    peers &= ((d >> bit) & 1) ? b : ~b;
+  }
+  return peers;
+}
+
+// Per-block digit counts: all keys of the lane are loaded first (one batch of
+// independent loads), then each group of lanes with equal digits adds its
+// size once.
 __global__ __launch_bounds__(kSortThreads) void sort_hist_kernel(SortPassArgs a) {
   __shared__ int h[kSortBuckets];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
   if (threadIdx.x < kSortBuckets) h[threadIdx.x] = 0;
+  const long long e0 = (long long)blockIdx.x * kSortBlock + (long long)w * 64 * kSortRounds + lane;
+  int key[kSortRounds];
+#pragma unroll
+  for (int r = 0; r < kSortRounds; ++r) key[r] = e0 + r * 64 < a.n ? a.keys_in[e0 + r * 64] : 0;
   __syncthreads();
-  const long long e0 = (long long)blockIdx.x * kSortBlock;
-  for (int i = threadIdx.x; i < kSortBlock; i += kSortThreads) {
-    const long long e = e0 + i;
-    if (e < a.n) atomicAdd(&h[sort_digit(a.keys_in[e], a.shift)], 1);
+  const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int r = 0; r < kSortRounds; ++r) {
+    const bool ok = e0 + r * 64 < a.n;
+    const int d = sort_digit(key[r], a.shift);
+    const unsigned long long peers = sort_peers(d, ok);
+    if (ok && (peers & lt) == 0) atomicAdd(&h[d], __builtin_popcountll(peers));
   }
   __syncthreads();
   if (threadIdx.x < kSortBuckets) a.hist[(size_t)threadIdx.x * a.B + blockIdx.x] = h[threadIdx.x];
 }
 
-// One workgroup: in-place exclusive scan of the 64 * B counts.
+// One workgroup: in-place exclusive scan of the 64 * B counts, in chunks that
+// are staged in LDS with coalesced loads and stores.
 __global__ __launch_bounds__(kSortScanThreads) void sort_scan_kernel(int* hist, int total) {
-  __shared__ int part[kSortScanThreads];
-  const int per = (total + kSortScanThreads - 1) / kSortScanThreads;
-  const int lo = threadIdx.x * per;
-  const int hi = lo + per < total ? lo + per : total;
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += hist[i];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the per-thread sums
-  for (int o = 1; o < kSortScanThreads; o <<= 1) {
-    const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+  constexpr int kPer = 16;
+  constexpr int kChunk = kSortScanThreads * kPer;
+  constexpr int kWaves = kSortScanThreads / 64;
+  __shared__ int buf[kChunk];
+  __shared__ int wsum[kWaves];
+  __shared__ int carry_s;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (threadIdx.x == 0) carry_s = 0;
+  for (int c0 = 0; c0 < total; c0 += kChunk) {
     __syncthreads();
-    part[threadIdx.x] += v;
+    {
+      int t[kPer];   // all loads of the chunk in flight at once
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = c0 + j * kSortScanThreads + threadIdx.x;
+        t[j] = i < total ? hist[i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) buf[j * kSortScanThreads + threadIdx.x] = t[j];
+    }
     __syncthreads();
-  }
-  int run = part[threadIdx.x] - s;   // exclusive prefix of this thread's range
-  for (int i = lo; i < hi; ++i) {
-    const int c = hist[i];
-    hist[i] = run;
-    run += c;
+    // each thread scans its kPer consecutive entries
+    int v[kPer], s = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      v[j] = s;
+      s += buf[threadIdx.x * kPer + j];
+    }
+    // inclusive scan of the thread sums within the wave, then across waves
+    int x = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int before = carry_s;
+    for (int i = 0; i < wv; ++i) before += wsum[i];
+    before += x - s;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) buf[threadIdx.x * kPer + j] = before + v[j];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = c0 + j * kSortScanThreads + threadIdx.x;
+      if (i < total) hist[i] = buf[j * kSortScanThreads + threadIdx.x];
+    }
+    if (threadIdx.x == kSortScanThreads - 1) carry_s = before + s;
   }
 }
 
@@ -66,13 +119,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(SortPassArgs
   for (int r = 0; r < kSortRounds; ++r) {
     const bool ok = e0 + r * 64 < a.n;
     const int d = sort_digit(key[r], a.shift);
-    // lanes holding the same digit: intersect the six bit ballots
-    unsigned long long peers = __builtin_amdgcn_ballot_w64(ok);
-#pragma unroll
-    for (int bit = 0; bit < kSortDigitBits; ++bit) {
-      const unsigned long long b = __builtin_amdgcn_ballot_w64(((d >> bit) & 1) != 0);
-      peers &= ((d >> bit) & 1) ? b : ~b;
-    }
+    const unsigned long long peers = sort_peers(d, ok);   // lanes holding the same digit
     const int rank = __builtin_popcountll(peers & lt);
     // the wave's LDS operations complete in issue order: every lane reads the
     // running count before its group's first lane raises it

@@ -9,11 +9,12 @@
 //
 // Design (HBM-bound, no MFMA work): an LSD radix sort on 6-bit digits of the
 // expert index (two passes for M <= 4096), each pass three kernels:
-//   sort_hist_kernel     per-block digit histogram (64 bins, LDS atomics),
+//   sort_hist_kernel     per-block digit histogram (64 bins; one LDS atomic
+//                        per group of equal digits in a wave round),
 //                        written digit-major: hist[d * B + b];
 //   sort_scan_kernel     one workgroup: exclusive scan of hist in (d, b)
-//                        order -> the first output position of digit d's
-//                        elements from block b;
+//                        order, staged through LDS -> the first output
+//                        position of digit d's elements from block b;
 //   sort_scatter_kernel  the block's elements are ranked stably within the
 //                        block with wave ballots (a 64-way multisplit: six
 //                        ballots give each lane the mask of lanes with its
@@ -31,7 +32,7 @@
 namespace more {
 
 constexpr int kSortThreads = 256;                 // 4 waves
-constexpr int kSortRounds = 32;                   // elements per lane
+constexpr int kSortRounds = 16;                   // elements per lane
 constexpr int kSortBlock = kSortThreads * kSortRounds;   // elements per block
 constexpr int kSortDigitBits = 6;
 constexpr int kSortBuckets = 1 << kSortDigitBits;

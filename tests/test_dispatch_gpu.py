@@ -45,7 +45,7 @@ def check(oracle_lib, idx, M, label):
 @pytest.mark.parametrize("N,M,k", [
     (1, 4096, 8),          # a single token
     (1000, 4096, 8),       # two radix passes, one block
-    (8192 // 8 + 3, 4096, 8),   # just over one block of 8192 entries
+    (4096 // 8 + 3, 4096, 8),   # just over one block of 4096 entries
     (5000, 64, 4),         # one pass (6-bit experts)
     (5000, 65, 4),         # two passes, the second with one live bit
     (3000, 1, 1),          # a single expert
