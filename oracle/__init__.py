@@ -9,16 +9,17 @@ Method: "MoRE: Scaling mixture of experts with hardware-aware low-rank routing",
 Algorithm 1 and Fig. 12 (exact top-k, softmax over the k selected logits),
 App. F.2.1 eq. (6) (full softmax / log-sum-exp), eq. (7) and (9) (column sums
 of the full softmax and the Switch balancing loss), App. G.1 (normalised
-routing entropy), App. E Fig. 9 (expert dispatch: sort + count).  The router
+routing entropy), App. F.2.2 eq. (10)-(12) and Algorithm 3 (the backward
+pass), App. E Fig. 9 (expert dispatch: sort + count).  The router
 arithmetic lives in ``more_oracle.c`` (plain C, fp64, OpenMP over tokens),
 which this package builds with gcc and calls through ctypes; the balancing
 statistics' final formulas and the dispatch sort are plain numpy in
 ``oracle.py``.
 """
-from .oracle import (DT_BF16, DT_F32, DT_F64, GATE_FULL, GATE_TOPK, balance_lowrank, balance_stats,
-                     build, dispatch_sort, library_path, logits, max_threads, route_fullrank, route_lowrank,
+from .oracle import (DT_BF16, DT_F32, DT_F64, GATE_FULL, GATE_TOPK, backward_lowrank, balance_lowrank,
+                     balance_stats, build, dispatch_sort, library_path, logits, max_threads, route_fullrank, route_lowrank,
                      softmax_colsum)
 
-__all__ = ["DT_BF16", "DT_F32", "DT_F64", "GATE_FULL", "GATE_TOPK", "balance_lowrank", "balance_stats",
+__all__ = ["DT_BF16", "DT_F32", "DT_F64", "GATE_FULL", "GATE_TOPK", "backward_lowrank", "balance_lowrank", "balance_stats",
            "build", "dispatch_sort", "library_path", "logits", "max_threads", "route_fullrank", "route_lowrank",
            "softmax_colsum"]

@@ -36,6 +36,11 @@
  * Balancing statistics (App. F.2.1, eq. (7)): psum_i = sum over tokens of the
  * full-softmax probability P_{n,i} = exp(l_{n,i} - m_n) / Z_n of eq. (6),
  * with m_n and Z_n taken over all M experts of the biased logits.
+ * Backward (App. F.2.2, eq. (10)-(12), Algorithm 3), per token n with the
+ * selection idx held fixed: g_n = sum_i pbar_i P_{n,i};
+ * ybar_{n,j} = P_{n,j} (pbar_j - g_n) + sum of tvbar_{n,c} over the slots c
+ * with idx_{n,c} = j; zbar = ybar R2^T; xbar = zbar R1^T; summed over tokens:
+ * R2bar += z^T ybar, R1bar += x^T zbar, bbar += ybar.
  * No blocking, fusion or reordering beyond these definitions.
  */
 #include <math.h>
@@ -278,6 +283,92 @@ int oracle_softmax_colsum(int dt, const void* X, int64_t N, int64_t h, const voi
     free(xs);
     free(zs);
     free(ls);
+    return OR_OK;
+}
+
+/*
+ * Gradients of F = sum_{n,c} tvbar_{n,c} l_{n, idx_{n,c}} + sum_i pbar_i psum_i
+ * (the prediction loss through the selected logits and the balancing loss
+ * through psum, eq. (9)-(12)) with respect to X, R1, R2 and the bias, the
+ * selection idx held fixed.  pbar may be NULL (zero).  Outputs (fp64):
+ * xbar N x h, r1bar h x r, r2bar r x M, bbar M.
+ */
+int oracle_backward_lowrank(int dt, const void* X, int64_t N, int64_t h, const void* R1, int64_t r,
+                            const void* R2, int64_t M, const float* bias, int k, const int32_t* idx,
+                            const double* tvbar, const double* pbar, double* xbar, double* r1bar,
+                            double* r2bar, double* bbar, int nthreads) {
+    if (dt < OR_DT_BF16 || dt > OR_DT_F64 || !X || !R1 || !R2 || !idx || !tvbar || !xbar || !r1bar || !r2bar ||
+        !bbar)
+        return OR_ERR_ARG;
+    if (N < 0 || h < 1 || M < 1 || r < 1 || k < 1 || k > M) return OR_ERR_ARG;
+    for (int64_t i = 0; i < N * k; ++i)
+        if (idx[i] < 0 || idx[i] >= M) return OR_ERR_ARG;
+    int T = 1;
+#ifdef _OPENMP
+    T = nthreads > 0 ? nthreads : omp_get_max_threads();
+#endif
+    (void)nthreads;
+    const size_t per = (size_t)(h * r + r * M + M);
+    double* part = (double*)calloc((size_t)T * per, sizeof(double));
+    double* work = (double*)malloc(sizeof(double) * (size_t)T * (size_t)(h + 2 * r + 2 * M));
+    if (!part || !work) {
+        free(part);
+        free(work);
+        return OR_ERR_NOMEM;
+    }
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(T) schedule(static)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        int t = 0;
+#ifdef _OPENMP
+        t = omp_get_thread_num();
+#endif
+        double* x = work + (size_t)t * (size_t)(h + 2 * r + 2 * M);
+        double* z = x + h;
+        double* zb = z + r;
+        double* l = zb + r;
+        double* yb = l + M;
+        double* r1b = part + (size_t)t * per;
+        double* r2b = r1b + h * r;
+        double* bb = r2b + r * M;
+        token_logits(dt, X, n, h, R1, r, R2, M, bias, 0, x, z, l);
+        double m = l[0];
+        for (int64_t i = 1; i < M; ++i) m = l[i] > m ? l[i] : m;
+        double Z = 0.0;
+        for (int64_t i = 0; i < M; ++i) Z += exp(l[i] - m);
+        double g = 0.0;
+        for (int64_t i = 0; i < M; ++i) {
+            yb[i] = exp(l[i] - m) / Z;   /* P_{n,i} for now */
+            g += (pbar ? pbar[i] : 0.0) * yb[i];
+        }
+        for (int64_t i = 0; i < M; ++i) yb[i] = yb[i] * ((pbar ? pbar[i] : 0.0) - g);
+        for (int c = 0; c < k; ++c) yb[idx[n * k + c]] += tvbar[n * k + c];
+        for (int64_t j = 0; j < r; ++j) {
+            double s = 0.0;
+            for (int64_t i = 0; i < M; ++i) s += yb[i] * load_elem(dt, R2, j * M + i);
+            zb[j] = s;
+        }
+        for (int64_t i = 0; i < h; ++i) {
+            double s = 0.0;
+            for (int64_t j = 0; j < r; ++j) s += zb[j] * load_elem(dt, R1, i * r + j);
+            xbar[n * h + i] = s;
+        }
+        for (int64_t i = 0; i < h; ++i)
+            for (int64_t j = 0; j < r; ++j) r1b[i * r + j] += x[i] * zb[j];
+        for (int64_t j = 0; j < r; ++j)
+            for (int64_t i = 0; i < M; ++i) r2b[j * M + i] += z[j] * yb[i];
+        for (int64_t i = 0; i < M; ++i) bb[i] += yb[i];
+    }
+    for (size_t q = 0; q < per; ++q) {
+        double s = 0.0;
+        for (int t = 0; t < T; ++t) s += part[(size_t)t * per + q];
+        if (q < (size_t)(h * r)) r1bar[q] = s;
+        else if (q < (size_t)(h * r + r * M)) r2bar[q - (size_t)(h * r)] = s;
+        else bbar[q - (size_t)(h * r + r * M)] = s;
+    }
+    free(part);
+    free(work);
     return OR_OK;
 }
 

@@ -50,8 +50,10 @@ def _load():
                                               p, p, p, p, p, p, p, i32]
         lib.oracle_logits.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, p]
         lib.oracle_softmax_colsum.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, p, i32]
+        lib.oracle_backward_lowrank.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, p, p, p,
+                                                p, p, p, p, i32]
         for f in (lib.oracle_route_lowrank, lib.oracle_route_fullrank, lib.oracle_logits,
-                  lib.oracle_softmax_colsum):
+                  lib.oracle_softmax_colsum, lib.oracle_backward_lowrank):
             f.restype = C.c_int
         lib.oracle_max_threads.restype = C.c_int
         _lib = lib
@@ -186,6 +188,26 @@ def balance_lowrank(X, R1, R2, bias, k: int, gate: int = GATE_TOPK, nthreads: in
     out["psum"] = softmax_colsum(X, R1, R2, bias, False, nthreads)
     out["counts"] = np.bincount(out["idx"].reshape(-1), minlength=M).astype(np.int64)
     out["lbal"], out["hnorm"] = balance_stats(out["psum"], out["counts"], N, k) if N > 0 else (0.0, 0.0)
+    return out
+
+
+def backward_lowrank(X, R1, R2, bias, idx, tvbar, pbar, nthreads: int = 0) -> dict:
+    """Gradients of F = sum tvbar * l[n, idx] + sum pbar * psum (App. F.2.2,
+    eq. 10-12, Algorithm 3) with the selection idx held fixed: dict(xbar
+    N x h, r1bar h x r, r2bar r x M, bbar M), all fp64."""
+    X, R1, R2 = (np.ascontiguousarray(a) for a in (X, R1, R2))
+    dt = _dt_code(X)
+    N, h = X.shape
+    r, M = R2.shape
+    k = idx.shape[1]
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    tv = np.ascontiguousarray(tvbar, dtype=np.float64)
+    pb = None if pbar is None else np.ascontiguousarray(pbar, dtype=np.float64)
+    out = dict(xbar=np.empty((N, h)), r1bar=np.empty((h, r)), r2bar=np.empty((r, M)), bbar=np.empty(M))
+    _check(_load().oracle_backward_lowrank(dt, _ptr(X), N, h, _ptr(R1), r, _ptr(R2), M, _ptr(b), k, _ptr(idx),
+                                           _ptr(tv), _ptr(pb), _ptr(out["xbar"]), _ptr(out["r1bar"]),
+                                           _ptr(out["r2bar"]), _ptr(out["bbar"]), nthreads))
     return out
 
 
