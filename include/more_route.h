@@ -204,6 +204,41 @@ more_status more_dispatch_sort(const int32_t* topk_idx, int64_t N, int32_t k, in
 size_t more_dispatch_workspace_bytes(int64_t N, int32_t k, int64_t M);
 
 /*
+ * Backward pass of the low-rank router with recompute (App. F.2.2, eq. (10)-
+ * (12), Algorithm 3).  With the forward's selection held fixed, it returns the
+ * gradients of F = sum_{n,j} tvbar[n,j] l[n, idx[n,j]] + sum_i pbar_i psum_i:
+ *   g_n = sum_i pbar_i P_{n,i}, P = exp(l - lse),
+ *   ybar_{n,e} = P_{n,e} (pbar_e - g_n) + tvbar[n,j] where idx[n,j] = e,
+ *   X_grad = (ybar R2^T) R1^T, R1_grad = X^T (ybar R2^T), R2_grad = z^T ybar,
+ *   bias_grad = sum over tokens of ybar   (z = X R1).
+ * Against weights packed by more_lowrank_pack (same R1, R2, bias):
+ *   X, R1, R2       the forward's inputs (bf16; R1 h x r, R2 r x M).
+ *   topk_idx        N x k int32: the forward's selection.
+ *   topk_logit_grad N x k fp32: gradient on the selected logits (tvbar).
+ *   psum_grad       M fp32 or NULL (zero): gradient on psum (pbar; for the
+ *                   Switch loss of eq. (9), pbar_i = (M / N) f_i).
+ *   lse             N fp32: the forward's log-sum-exp (balancing call).
+ *   X_grad          N x h bf16 (required).  R1_grad h x r, R2_grad r x M
+ *                   fp32 (required).  bias_grad M fp32 or NULL.
+ *   workspace       at least more_backward_workspace_bytes(...) bytes: the
+ *                   packed weights, then the token scratch and the backward's
+ *                   intermediates (overwritten).
+ * Envelope: bf16, r in {16, 32}, h % 32 == 0, k <= 32, M <= 16384 and R1
+ * small enough for the projection kernel's LDS; other shapes return
+ * MORE_ERR_UNSUPPORTED.  Sums over tokens run in a fixed order (the same
+ * inputs give the same bits).  N = 0 is a no-op.
+ */
+more_status more_lowrank_backward_packed(more_dtype dt, const void* X, int64_t N, int64_t h, const void* R1,
+                                         int64_t r, const void* R2, int64_t M, int32_t k, const int32_t* topk_idx,
+                                         const float* topk_logit_grad, const float* psum_grad, const float* lse,
+                                         void* X_grad, float* R1_grad, float* R2_grad, float* bias_grad,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of more_lowrank_backward_packed (0 outside its envelope).
+ * Pure host function, no HIP call. */
+size_t more_backward_workspace_bytes(more_dtype dt, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k);
+
+/*
  * Fused standard (full-rank) router + top-k + gates: the same selection and
  * gates with l = x W + b (§2 standard router; App. H.3 Fig. 20 fuses it the
  * same way, reloading weight tiles instead of a rank-r intermediate).

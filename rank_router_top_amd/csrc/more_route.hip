@@ -21,6 +21,7 @@
 #include "more_dispatch.h"
 #include "more_balance.h"
 #include "more_sort.h"
+#include "more_backward.h"
 
 using namespace more;
 
@@ -548,6 +549,156 @@ more_status more_lowrank_balance_packed(more_dtype dt, const void* X, int64_t N,
   ta.k = k;
   ta.M = (int)M;
   return launch_balance(L.r16, pa, ca, sa, ta, hs) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+}
+
+namespace {
+// Workspace of the backward call: packed weights, z scratch for N tokens,
+// then the backward's own area.
+struct BwdLayout {
+  size_t off_z, off_pbq, off_pbpos, off_r2b, off_r2t, off_inv, off_g, off_zbar, off_zrm, off_r2part, off_bpart,
+      off_r1part, total;
+  int slotsE, slotsX, GE, GX;
+};
+bool backward_layout(more_dtype dt, const Layout& L, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k,
+                     BwdLayout* B) {
+  if (dt != MORE_DT_BF16 || L.ksq <= 0 || L.r16 > 2 || r % 16 != 0 || h % kTile != 0 || k > 32) return false;
+  if (L.Mpad > 16384) return false;   // bias + pbar of every tile stay in the token kernel's LDS
+  int ksp = 0;
+  bool tail = false;
+  proj_ksteps(h, L.r16, &ksp, &tail);
+  if ((long long)proj_lds_bytes(L.r16, ksp) > kLdsBytes) return false;
+  const int64_t nb = N > 0 ? (N + kTile - 1) / kTile : 0;
+  B->slotsE = (int)std::min<int64_t>(kBwdSlots, std::max<int64_t>(nb, 1));
+  B->slotsX = B->slotsE;
+  B->GE = (L.NT + kBwdExpWaves * kBwdExpTiles - 1) / (kBwdExpWaves * kBwdExpTiles);
+  B->GX = (int)((h / kTile + kBwdXWaves * kBwdXTiles - 1) / (kBwdXWaves * kBwdXTiles));
+  const size_t nrow = (size_t)std::max<int64_t>(nb, 1) * kTile;
+  size_t off = L.total;
+  B->off_z = off;
+  off += z_scratch_bytes(dt, L, N);
+  B->off_pbq = off;
+  off += align_up((size_t)L.NT * 32 * sizeof(float));
+  B->off_pbpos = off;
+  off += align_up((size_t)L.Mpad * sizeof(float));
+  B->off_r2b = off;
+  off += align_up((size_t)L.NT * 2048);
+  B->off_r2t = off;
+  off += align_up((size_t)M * kBwdRow * 2);
+  B->off_inv = off;
+  off += align_up((size_t)M * sizeof(int));
+  B->off_g = off;
+  off += align_up(nrow * sizeof(float));
+  B->off_zbar = off;
+  off += align_up(nrow * kBwdRow * sizeof(float));
+  B->off_zrm = off;
+  off += align_up(nrow * kBwdRow * sizeof(float));
+  B->off_r2part = off;
+  off += align_up((size_t)B->slotsE * kBwdRow * L.Mpad * sizeof(float));
+  B->off_bpart = off;
+  off += align_up((size_t)B->slotsE * L.Mpad * sizeof(float));
+  B->off_r1part = off;
+  off += align_up((size_t)B->slotsX * (size_t)h * kBwdRow * sizeof(float));
+  B->total = off;
+  return true;
+}
+}  // namespace
+
+size_t more_backward_workspace_bytes(more_dtype dt, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k) {
+  if (more_route_workspace_bytes(0, dt, N, h, r, M, k, MORE_GATE_TOPK_SOFTMAX, 0) == 0) return 0;
+  Layout L;
+  make_layout(0, dt, h, r, M, &L);
+  BwdLayout B;
+  return backward_layout(dt, L, N, h, r, M, k, &B) ? B.total : 0;
+}
+
+more_status more_lowrank_backward_packed(more_dtype dt, const void* X, int64_t N, int64_t h, const void* R1,
+                                         int64_t r, const void* R2, int64_t M, int32_t k, const int32_t* topk_idx,
+                                         const float* topk_logit_grad, const float* psum_grad, const float* lse,
+                                         void* X_grad, float* R1_grad, float* R2_grad, float* bias_grad,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  more_status st = validate(0, dt, X, N, h, R1, r, R2, M, nullptr, k, MORE_GATE_TOPK_SOFTMAX, topk_idx,
+                            topk_logit_grad, nullptr, lse);
+  if (st != MORE_OK || N == 0) return st;
+  if (!lse || !X_grad || !R1_grad || !R2_grad) return MORE_ERR_NULL_ARG;
+  if (!aligned16(X_grad) || !aligned16(R1_grad) || !aligned16(R2_grad) || (psum_grad && !aligned16(psum_grad)) ||
+      (bias_grad && !aligned16(bias_grad)))
+    return MORE_ERR_ALIGNMENT;
+  Layout L;
+  make_layout(0, dt, h, r, M, &L);
+  BwdLayout B;
+  if (!backward_layout(dt, L, N, h, r, M, k, &B)) return MORE_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < B.total || ((uintptr_t)workspace % kAlign) != 0) return MORE_ERR_WORKSPACE;
+  const int64_t nb = (N + kTile - 1) / kTile;
+  if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
+  char* ws = (char*)workspace;
+  hipStream_t hs = (hipStream_t)stream;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MORE_ERR_HIP;
+  // 1. recompute z (Algorithm 3, phase 1) into the token scratch
+  int ksp = 0;
+  bool tail = false;
+  proj_ksteps(h, L.r16, &ksp, &tail);
+  const size_t pj_lds = proj_lds_bytes(L.r16, ksp);
+  proj_fn pf = pick_proj(L.r16, tail);
+  if (hipFuncSetAttribute((const void*)pf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pj_lds) != hipSuccess)
+    return MORE_ERR_HIP;
+  ProjArgs pa;
+  pa.X = X;
+  pa.N = N;
+  pa.h = (int)h;
+  pa.R1q = ws + L.off_r1q;
+  pa.KSQ = std::min(L.ksq, ksp);
+  pa.KSP = ksp;
+  pa.NB = (int)nb;
+  pa.Z = ws + B.off_z;
+  pa.spin_limit = 1 << 22;
+  const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kProjWaves - 1) / kProjWaves));
+  hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, hs, pa);
+  if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
+  // 2. phase 2 (two sweeps) and phase 3
+  BwdArgs a;
+  memset(&a, 0, sizeof a);
+  a.Z = ws + B.off_z;
+  a.lse = lse;
+  a.R2p = ws + L.off_r2p;
+  a.biasp = (const float*)(ws + L.off_bias);
+  a.perm = (const int*)(ws + L.off_perm);
+  a.X = (const uint16_t*)X;
+  a.R1 = (const uint16_t*)R1;
+  a.R2 = (const uint16_t*)R2;
+  a.idx = topk_idx;
+  a.tv = topk_logit_grad;
+  a.pbar = psum_grad;
+  a.pbq = (float*)(ws + B.off_pbq);
+  a.pbpos = (float*)(ws + B.off_pbpos);
+  a.R2b = (uint16_t*)(ws + B.off_r2b);
+  a.R2t = (uint16_t*)(ws + B.off_r2t);
+  a.invpos = (int*)(ws + B.off_inv);
+  a.g = (float*)(ws + B.off_g);
+  a.zbar = (float*)(ws + B.off_zbar);
+  a.zrm = (float*)(ws + B.off_zrm);
+  a.r2part = (float*)(ws + B.off_r2part);
+  a.bpart = (float*)(ws + B.off_bpart);
+  a.r1part = (float*)(ws + B.off_r1part);
+  a.xbar = (uint16_t*)X_grad;
+  a.r1grad = R1_grad;
+  a.r2grad = R2_grad;
+  a.bgrad = bias_grad;
+  a.N = N;
+  a.h = (int)h;
+  a.r = (int)r;
+  a.M = (int)M;
+  a.k = k;
+  a.NT = L.NT;
+  a.NB = (int)nb;
+  a.slotsE = B.slotsE;
+  a.GE = B.GE;
+  a.slotsX = B.slotsX;
+  a.GX = B.GX;
+  const size_t tok_lds = (size_t)L.NT * 32 * sizeof(float) * 2;
+  return launch_backward(L.r16, a, tok_lds, cus, hs) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 
 size_t more_dispatch_workspace_bytes(int64_t N, int32_t k, int64_t M) {

@@ -147,3 +147,19 @@ def make_expert_sets(seed: int, cfg_id: int, N: int, M: int, k: int, skew: float
                 out[i] = rng.permutation(M)[:k]
         else:
             out[bad] = draw(bad.size)
+
+
+TENSOR_GRAD = 6
+
+
+def make_grads(seed: int, cfg_id: int, N: int, k: int, M: int) -> tuple[np.ndarray, np.ndarray]:
+    """Incoming gradients of a backward pass: tvbar (N x k fp32) ~ N(0, 1) on
+    the selected logits, and pbar (M fp32) = (M / N) f + N(0, 0.1 M / N): the
+    Switch-loss gradient of a skewed dispatch (f drawn like make_expert_sets'
+    loads) plus noise."""
+    rng = _rng(seed, cfg_id, TENSOR_GRAD)
+    tv = rng.standard_normal((N, k)).astype(np.float32)
+    f = np.exp(0.7 * rng.standard_normal(M))
+    f = f / f.sum()
+    pb = ((M / max(N, 1)) * (f + 0.1 * rng.standard_normal(M) / M)).astype(np.float32)
+    return tv, pb

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "MORE_OK", 1: "MORE_ERR_NULL_ARG", 2: "MORE_ERR_BAD_SHAPE", 3
 EXPORTS = ("more_route_lowrank", "more_route_fullrank", "more_route_workspace_bytes",
            "more_status_str", "more_abi_version", "more_lowrank_pack", "more_lowrank_route_packed",
            "more_lowrank_balance_packed", "more_balance_workspace_bytes", "more_dispatch_sort",
-           "more_dispatch_workspace_bytes")
+           "more_dispatch_workspace_bytes", "more_lowrank_backward_packed", "more_backward_workspace_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -65,6 +65,11 @@ def lib() -> C.CDLL:
             L.more_dispatch_sort.argtypes = [p, i64, i32, i64, p, p, p, p, C.c_size_t, p]
             L.more_dispatch_sort.restype = C.c_int
             L.more_dispatch_workspace_bytes.argtypes = [i64, i32, i64]
+            L.more_lowrank_backward_packed.argtypes = [i32, p, i64, i64, p, i64, p, i64, i32, p, p, p, p,
+                                                       p, p, p, p, p, C.c_size_t, p]
+            L.more_lowrank_backward_packed.restype = C.c_int
+            L.more_backward_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i32]
+            L.more_backward_workspace_bytes.restype = C.c_size_t
             L.more_dispatch_workspace_bytes.restype = C.c_size_t
             L.more_balance_workspace_bytes.restype = C.c_size_t
             L.more_route_workspace_bytes.argtypes = [C.c_int, i32, i64, i64, i64, i64, i32, i32, C.c_int]
@@ -208,6 +213,33 @@ def dispatch_sort(idx, M: int, *, out=None, workspace=None, stream=None) -> dict
     _check("more_dispatch_sort", lib().more_dispatch_sort(
         _ptr(idx), N, k, M, _ptr(out["sorted_expert"]), _ptr(out["sorted_slot"]), _ptr(out["offsets"]),
         _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def backward_workspace_bytes(dt: int, N: int, h: int, r: int, M: int, k: int) -> int:
+    return int(lib().more_backward_workspace_bytes(dt, N, h, r, M, k))
+
+
+def backward_lowrank_packed(X, R1, R2, idx, logit_grad, psum_grad, lse, workspace, *, out=None,
+                            want_bias_grad: bool = True, stream=None) -> dict:
+    """more_lowrank_backward_packed: gradients of the selected-logit and psum
+    losses with the selection held fixed, against weights packed by
+    pack_lowrank into `workspace` (sized by backward_workspace_bytes).
+    Returns dict(X_grad bf16 N x h, R1_grad, R2_grad, bias_grad)."""
+    import torch
+    dt = _dtype_code(X)
+    N, h = X.shape
+    r, M = R2.shape
+    k = idx.shape[1]
+    if out is None:
+        out = dict(X_grad=torch.empty((N, h), dtype=torch.bfloat16, device=X.device),
+                   R1_grad=torch.empty((h, r), dtype=torch.float32, device=X.device),
+                   R2_grad=torch.empty((r, M), dtype=torch.float32, device=X.device),
+                   bias_grad=torch.empty((M,), dtype=torch.float32, device=X.device) if want_bias_grad else None)
+    _check("more_lowrank_backward_packed", lib().more_lowrank_backward_packed(
+        dt, _ptr(X), N, h, _ptr(R1), r, _ptr(R2), M, k, _ptr(idx), _ptr(logit_grad), _ptr(psum_grad), _ptr(lse),
+        _ptr(out["X_grad"]), _ptr(out["R1_grad"]), _ptr(out["R2_grad"]), _ptr(out.get("bias_grad")),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 
