@@ -21,6 +21,10 @@ resident in HBM.  Prints ONE JSON line:
                  (more_lowrank_balance_packed: routing with the full-softmax
                  normaliser, then the second sweep for psum, the dispatch
                  counts, L_bal and H_norm) on the same tokens, HIP-event timed
+  backward       the backward pass (more_lowrank_backward_packed, Alg. 3) on
+                 the same tokens with the routing call's selection, seeded
+                 incoming gradients and the balancing call's lse, HIP-event
+                 timed, against its HBM bound (read X once, write X_grad)
   dispatch       the expert dispatch (more_dispatch_sort: the N x k indices
                  the routing call returned -> expert-sorted slots + offsets),
                  HIP-event timed, algorithmic bytes (read N k indices, write
@@ -76,6 +80,7 @@ def parse():
     ap.add_argument("--no-fullrank", action="store_true")
     ap.add_argument("--no-balance", action="store_true")
     ap.add_argument("--no-dispatch", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--fullrank-steps", type=int, default=3)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, "
@@ -323,6 +328,39 @@ def main():
             "L_bal": st[0], "H_norm": st[1],
             "exp_count_per_call": 2 * cfg.N * cfg.M,
             "exp_bound_ms_per_call": 2 * cfg.N * cfg.M / EXP_PEAK_PER_S * 1e3}
+        if not args.no_backward:
+            nbw = R.backward_workspace_bytes(dt, cfg.N, cfg.h, cfg.r, cfg.M, cfg.k)
+            if nbw > 0:
+                from rank_router_top_amd import inputs as I
+                wsw_b = torch.empty(max(nbw, nbb), dtype=torch.uint8, device=dev)
+                R.pack_lowrank(R1, R2, b, wsw_b, stream=stream)
+                R.balance_lowrank_packed(X, cfg.r, cfg.M, cfg.k, gate, wsw_b, out=bout, stream=stream)
+                tv_np, pb_np = I.make_grads(args.seed, 73, cfg.N, cfg.k, cfg.M)
+                tv_t = torch.from_numpy(tv_np).to(dev)
+                pb_t = torch.from_numpy(pb_np).to(dev)
+                gout = dict(X_grad=torch.empty((cfg.N, cfg.h), dtype=torch.bfloat16, device=dev),
+                            R1_grad=torch.empty((cfg.h, cfg.r), dtype=torch.float32, device=dev),
+                            R2_grad=torch.empty((cfg.r, cfg.M), dtype=torch.float32, device=dev),
+                            bias_grad=torch.empty((cfg.M,), dtype=torch.float32, device=dev))
+
+                def backward_call():
+                    R.backward_lowrank_packed(X, R1, R2, bout["idx"], tv_t, pb_t, bout["lse"], wsw_b, out=gout,
+                                              stream=stream)
+
+                for _ in range(2):
+                    backward_call()
+                w_mean, w_med, w_p10, w_p90 = time_events(torch, backward_call, max(args.steps // 2, 10), stream)
+                w_bytes = 2 * cfg.N * cfg.h * 2 + (cfg.h * cfg.r + cfg.r * cfg.M) * 2 * 2 + cfg.N * cfg.k * 12
+                w_ach = w_bytes / (w_mean * 1e-3) / 1e9
+                log(f"backward call mean {w_mean:.4f} ms (p10 {w_p10:.4f}, p90 {w_p90:.4f})")
+                result["backward"] = {
+                    "entry": "more_lowrank_backward_packed", "value": cfg.N / (w_mean * 1e-3), "unit": "tokens/s",
+                    "ms_per_call": w_mean, "ms_median": w_med, "ms_p10": w_p10, "ms_p90": w_p90,
+                    "exp_count_per_call": 3 * cfg.N * cfg.M,
+                    "mfma_flop_per_call": 2 * cfg.N * (3 * cfg.h * cfg.r + 4 * cfg.M * cfg.r),
+                    "roofline": {"bound": "hbm", "achieved": w_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": w_ach / HBM_PEAK_GBS, "algorithmic_bytes_per_call": w_bytes}}
+                del wsw_b, gout
         del wsb, bout
 
     if not args.no_dispatch:

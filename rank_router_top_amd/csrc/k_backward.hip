@@ -133,6 +133,7 @@ __global__ __launch_bounds__(64 * kBwdTokWaves) void bwd_tok_kernel(BwdArgs a) {
         int e = a.idx[n * a.k + c];
         e = e < 0 ? 0 : (e >= a.M ? a.M - 1 : e);
         const float w = a.tv[n * a.k + c];
+        if (hf == 0) a.selpos[n * a.k + c] = a.invpos[e] * 32 + tok;
         const uint16_t* col = a.R2t + (size_t)e * kBwdRow + 4 * hf;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(64 * kBwdTokWaves) void bwd_tok_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------- expert-stationary
-template <int R16>
+template <int R16, int NS>
 __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
   constexpr int TW = kBwdExpTiles;
   __shared__ __align__(16) float dt[kBwdExpWaves][kTile * kTile];   // per wave: ybar tile [expert col][token]
@@ -195,81 +196,91 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
     for (int v = 0; v < 16; ++v) r2acc[u][v] = 0.f;
     bacc[u] = 0.f;
   }
-  const int nsel = (kTile * a.k + 63) / 64;   // selections of a block per lane (k <= 32: <= 16)
-  for (long long j = s; j < a.NB; j += a.slotsE) {
-    __builtin_amdgcn_sched_barrier(0);
+  // selections of a block per lane: 32 k / 64 <= NS
+  const long long nk = a.N * a.k;
+  // loads of one token block (raw; masked where used)
+  struct Blk {
+    bf16x8 zh[R16], zl[R16];
+    float lr[16], gr[16], zt[16], sv[NS];
+    int sp[NS];
+  };
+  auto load_blk = [&](long long j, Blk& B) {
     const long long n0 = j * kTile;
     const rsrc_t zd = make_rsrc((const char*)a.Z + (size_t)j * z_block_bytes(R16), z_block_bytes(R16));
-    bf16x8 zh[R16], zl[R16];
 #pragma unroll
     for (int m = 0; m < R16; ++m) {
-      zh[m] = buf_load(zd, lane * 16 + m * 1024, 0);
-      zl[m] = buf_load(zd, lane * 16 + (R16 + m) * 1024, 0);
+      B.zh[m] = buf_load(zd, lane * 16 + m * 1024, 0);
+      B.zl[m] = buf_load(zd, lane * 16 + (R16 + m) * 1024, 0);
     }
-    // token of register v: 8(v/4) + 4hf + v%4; lse start (-inf past N) and g
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const long long tk = n0 + 8 * (v >> 2) + 4 * hf + (v & 3);
+      const long long tc = tk < a.N ? tk : a.N - 1;
+      B.lr[v] = a.lse[tc];
+      B.gr[v] = a.g[tc];
+      // z^T operand: K slot e' of step m = token 16m + 8(e'/4) + 4hf + e'%4, rank = col
+      const long long tz = n0 + 16 * (v >> 3) + 8 * ((v & 7) >> 2) + 4 * hf + (v & 3);
+      B.zt[v] = a.zrm[(tz < a.N ? tz : a.N - 1) * kBwdRow + col];
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      long long q = n0 * a.k + lane + 64 * i;
+      q = q < nk ? q : nk - 1;
+      B.sp[i] = a.selpos[q];
+      B.sv[i] = a.tv[q];
+    }
+  };
+  auto work = [&](long long j, const Blk& B) {
+    __builtin_amdgcn_sched_barrier(0);
+    const long long n0 = j * kTile;
     floatx16 c0;
     float gv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const long long tk = n0 + 8 * (v >> 2) + 4 * hf + (v & 3);
-      const long long tc = tk < a.N ? tk : a.N - 1;
-      const float ls = a.lse[tc], gg = a.g[tc];
-      c0[v] = tk < a.N ? -ls : -__builtin_inff();
-      gv[v] = gg;
+      c0[v] = tk < a.N ? -B.lr[v] : -__builtin_inff();
+      gv[v] = B.gr[v];
     }
-    // z^T operand of MFMA m: lane (rho, hf), K slot e' = token 16m + 8(e'/4) + 4hf + e'%4
     bf16x8 zth[2], ztl[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const long long tk = n0 + 16 * m + 8 * (e >> 2) + 4 * hf + (e & 3);
-        x[e] = tk < a.N ? a.zrm[tk * kBwdRow + col] : 0.f;
+        const long long tz = n0 + 16 * m + 8 * (e >> 2) + 4 * hf + (e & 3);
+        x[e] = tz < a.N ? B.zt[8 * m + e] : 0.f;
       }
       split8(x, zth[m], ztl[m]);
     }
-    // the block's selections: lane takes entries lane, lane + 64, ... of the
-    // 32 k (token, slot) pairs; position, and token within the block
-    int spos[16];
-    float sval[16];
+    int spos[NS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      spos[i] = -1;
-      sval[i] = 0.f;
-      if (i < nsel) {
-        const int q = lane + 64 * i;
-        const long long tk = n0 + q / a.k;
-        if (q < kTile * a.k && tk < a.N) {
-          int ex = a.idx[n0 * a.k + q];
-          ex = ex < 0 ? 0 : (ex >= a.M ? a.M - 1 : ex);   // out-of-range indices: no access outside the table
-          spos[i] = a.invpos[ex] * 32 + q / a.k;            // position * 32 + token
-          sval[i] = a.tv[n0 * a.k + q];
-        }
-      }
+    for (int i = 0; i < NS; ++i) {
+      const int q = lane + 64 * i;
+      const bool ok = q < kTile * a.k && n0 + q / a.k < a.N;
+      spos[i] = ok ? B.sp[i] : -1;
     }
 #pragma unroll
     for (int u = 0; u < TW; ++u) {
       const int t = t0 + u;
       floatx16 acc = c0;
 #pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(zh[m], w[u][m], acc);
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(B.zh[m], w[u][m], acc);
 #pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(zl[m], w[u][m], acc);
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(B.zl[m], w[u][m], acc);
       float d[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) d[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kLog2e, bl[u])) * (pb[u] - gv[v]);
       // selected (token, expert) pairs in this tile: add tvbar through the LDS tile
       bool hit = false;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) hit = hit || (i < nsel && (spos[i] >> 10) == t);
+      for (int i = 0; i < NS; ++i) hit = hit || (spos[i] >= 0 && (spos[i] >> 10) == t);
       if (any_lane(hit)) {
         float* row = my + col * kTile + 4 * hf;
 #pragma unroll
         for (int q = 0; q < 4; ++q) *(float4*)(row + 8 * q) = make_float4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (i < nsel && (spos[i] >> 10) == t) my[((spos[i] >> 5) & 31) * kTile + (spos[i] & 31)] += sval[i];
+        for (int i = 0; i < NS; ++i)
+          if (spos[i] >= 0 && (spos[i] >> 10) == t) my[((spos[i] >> 5) & 31) * kTile + (spos[i] & 31)] += B.sv[i];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 x = *(const float4*)(row + 8 * q);
@@ -292,6 +303,18 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
         r2acc[u] = mfma_bf16(ztl[m], hi, r2acc[u]);
       }
     }
+  };
+  Blk b0, b1;
+  const long long st = a.slotsE, last = a.NB - 1;
+  long long j = s;
+  load_blk(j, b0);
+  for (;; j += 2 * st) {
+    load_blk(j + st < last ? j + st : last, b1);
+    work(j, b0);
+    if (j + st >= a.NB) break;
+    load_blk(j + 2 * st < last ? j + 2 * st : last, b0);
+    work(j + st, b1);
+    if (j + 2 * st >= a.NB) break;
   }
   // partials: R2bar^T rows rho = 8(v/4) + 4hf + v%4, column = this lane's position
 #pragma unroll
@@ -310,93 +333,162 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------ X stream
+// Each wave owns HT h tiles (32 columns each) and walks the token blocks of
+// its slot, one block of loads ahead.  X rows arrive with 16-byte loads and
+// go into the wave's LDS area transposed ([column][token]), so the B operand
+// of R1bar^T += zbar^T X (K = the block's tokens) is one 16-byte LDS read.
+// xbar^T = R1 zbar^T leaves four consecutive columns of one token per lane
+// and register group; they are staged in LDS by token rows and leave with
+// 16-byte stores.
 template <int R16>
 __global__ __launch_bounds__(64 * kBwdXWaves) void bwd_x_kernel(BwdArgs a) {
   constexpr int HT = kBwdXTiles;
+  constexpr int WC = HT * kTile;                 // columns of one wave
+  constexpr int NCH = kTile * WC / 8 / 64;       // 16-byte chunks of a block slice per lane
+  __shared__ __align__(16) uint16_t xs_all[kBwdXWaves][WC * kTile];   // X^T [column][token]
+  __shared__ __align__(16) uint16_t ys_all[kBwdXWaves][kTile * WC];   // xbar [token][column]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int s = blockIdx.x / a.GX, gq = blockIdx.x % a.GX;
-  const int ht0 = (gq * kBwdXWaves + wave) * HT;   // first h tile of this wave
+  const int ht0 = (gq * kBwdXWaves + wave) * HT;
   const int nht = a.h / kTile;
   if (ht0 >= nht) return;
+  const int c0 = ht0 * kTile;
+  const int ncol = (nht - ht0 < HT ? nht - ht0 : HT) * kTile;
+  uint16_t* xs = xs_all[wave];
+  uint16_t* ys = ys_all[wave];
   const int hf = lane >> 5, col = lane & 31;
-  // R1^T operand of h tile u: lane (h column, hf), K slot e' = rank 16m + 8hf + e'
+  // R1 rows as the A operand of xbar^T: lane (column, hf), K slot e' = rank 16m + 8hf + e'
   bf16x8 br[HT][R16];
 #pragma unroll
   for (int u = 0; u < HT; ++u) {
-    const int hc = (ht0 + u < nht ? ht0 + u : nht - 1) * kTile + col;
+    const int hc = c0 + (u * kTile < ncol ? u * kTile : 0) + col;
 #pragma unroll
-    for (int m = 0; m < R16; ++m) br[u][m] = __builtin_bit_cast(bf16x8, *(const u32x4*)(a.R1 + (size_t)hc * a.r + 16 * m + 8 * hf));
+    for (int m = 0; m < R16; ++m)
+      br[u][m] = __builtin_bit_cast(bf16x8, *(const u32x4*)(a.R1 + (size_t)hc * a.r + 16 * m + 8 * hf));
   }
   floatx16 r1acc[HT];
 #pragma unroll
   for (int u = 0; u < HT; ++u)
 #pragma unroll
     for (int v = 0; v < 16; ++v) r1acc[u][v] = 0.f;
-  for (long long j = s; j < a.NB; j += a.slotsX) {
+  // loads of one block: X slice chunks (token q / (WC/8), 8 columns) and zbar
+  struct Blk {
+    u32x4 x[NCH];
+    float4 za[2 * R16];   // zbar row of token `col`, ranks 16m + 8hf .. +7
+    float zt[16];         // zbar[token 16m + 8hf + e][rank col]
+  };
+  auto load_blk = [&](long long j, Blk& B) {
     const long long n0 = j * kTile;
-    // zbar as the A operand of xbar (lane = token, K slot = rank 16m + 8hf + e')
-    // and of R1bar^T (lane = rank, K slot = token 16m + 8hf + e')
-    bf16x8 zah[R16], zal[R16], zth[2], ztl[2];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = lane + 64 * i;
+      const long long row = n0 + q / (WC / 8);
+      const int cc = (q % (WC / 8)) * 8;
+      const long long rr = row < a.N ? row : a.N - 1;
+      const int c = cc < ncol ? cc : 0;
+      B.x[i] = *(const u32x4*)(a.X + rr * a.h + c0 + c);   // rows / columns past the end: masked at use
+    }
+    const long long tk = n0 + col < a.N ? n0 + col : a.N - 1;
+#pragma unroll
+    for (int m = 0; m < R16; ++m) {
+      B.za[2 * m] = *(const float4*)(a.zbar + tk * kBwdRow + 16 * m + 8 * hf);
+      B.za[2 * m + 1] = *(const float4*)(a.zbar + tk * kBwdRow + 16 * m + 8 * hf + 4);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const long long tt = n0 + 16 * (e >> 3) + 8 * hf + (e & 7);
+      B.zt[e] = a.zbar[(tt < a.N ? tt : a.N - 1) * kBwdRow + col];
+    }
+  };
+  auto work = [&](long long j, const Blk& B) {
+    __builtin_amdgcn_sched_barrier(0);
+    const long long n0 = j * kTile;
+    // X slice -> LDS, transposed; rows past N and columns past the wave's end are zero
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = lane + 64 * i;
+      const int tok = q / (WC / 8);
+      const int cc = (q % (WC / 8)) * 8;
+      const bool ok = n0 + tok < a.N && cc < ncol;
+      const u32x4 v = B.x[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w32 = v[e >> 1];
+        xs[(cc + e) * kTile + tok] = ok ? (uint16_t)((e & 1) ? (w32 >> 16) : (w32 & 0xffff)) : (uint16_t)0;
+      }
+    }
+    const bool tok_ok = n0 + col < a.N;
+    bf16x8 zbh[R16], zbl[R16], zth[2], ztl[2];
 #pragma unroll
     for (int m = 0; m < R16; ++m) {
       float x[8];
-      const long long tk = n0 + col;
-      const float* zr = a.zbar + (tk < a.N ? tk : a.N - 1) * kBwdRow + 16 * m + 8 * hf;
-      const float4 p0 = *(const float4*)zr, p1 = *(const float4*)(zr + 4);
-      const bool ok = tk < a.N;
-      x[0] = ok ? p0.x : 0.f; x[1] = ok ? p0.y : 0.f; x[2] = ok ? p0.z : 0.f; x[3] = ok ? p0.w : 0.f;
-      x[4] = ok ? p1.x : 0.f; x[5] = ok ? p1.y : 0.f; x[6] = ok ? p1.z : 0.f; x[7] = ok ? p1.w : 0.f;
-      split8(x, zah[m], zal[m]);
+      const float4 p0 = B.za[2 * m], p1 = B.za[2 * m + 1];
+      x[0] = p0.x; x[1] = p0.y; x[2] = p0.z; x[3] = p0.w; x[4] = p1.x; x[5] = p1.y; x[6] = p1.z; x[7] = p1.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = tok_ok ? x[e] : 0.f;
+      split8(x, zbh[m], zbl[m]);
     }
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {   // the 32 tokens of the block: two K steps
+    for (int m = 0; m < 2; ++m) {
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const long long tt = n0 + 16 * m + 8 * hf + e;
-        y[e] = tt < a.N ? a.zbar[tt * kBwdRow + col] : 0.f;
-      }
+      for (int e = 0; e < 8; ++e) y[e] = n0 + 16 * m + 8 * hf + e < a.N ? B.zt[8 * m + e] : 0.f;
       split8(y, zth[m], ztl[m]);
     }
 #pragma unroll
     for (int u = 0; u < HT; ++u) {
-      if (ht0 + u >= nht) break;
-      const int hc = (ht0 + u) * kTile + col;
-      // xbar tile: rows = tokens 8(v/4) + 4hf + v%4, column = h
+      if (u * kTile >= ncol) break;
+      // xbar^T tile: rows = columns u*32 + 8(v/4) + 4hf + v%4, column = token
       floatx16 xa;
 #pragma unroll
       for (int v = 0; v < 16; ++v) xa[v] = 0.f;
 #pragma unroll
       for (int m = 0; m < R16; ++m) {
-        xa = mfma_bf16(zah[m], br[u][m], xa);
-        xa = mfma_bf16(zal[m], br[u][m], xa);
+        xa = mfma_bf16(br[u][m], zbh[m], xa);
+        xa = mfma_bf16(br[u][m], zbl[m], xa);
       }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const long long tk = n0 + 8 * (v >> 2) + 4 * hf + (v & 3);
-        if (tk < a.N) a.xbar[tk * a.h + hc] = bf16_bits(xa[v]);
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = (uint32_t)bf16_bits(xa[4 * q]) | ((uint32_t)bf16_bits(xa[4 * q + 1]) << 16);
+        const uint32_t hi = (uint32_t)bf16_bits(xa[4 * q + 2]) | ((uint32_t)bf16_bits(xa[4 * q + 3]) << 16);
+        *(uint2*)(ys + col * WC + u * kTile + 8 * q + 4 * hf) = make_uint2(lo, hi);
       }
       // R1bar^T partial: rows = ranks, column = h; K = the block's tokens
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        bf16x8 xb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const long long tt = n0 + 16 * m + 8 * hf + e;
-          const uint16_t bits = a.X[(tt < a.N ? tt : a.N - 1) * a.h + hc];
-          xb[e] = tt < a.N ? __builtin_bit_cast(bf16, bits) : (bf16)0.f;
-        }
+        const bf16x8 xb = __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + (u * kTile + col) * kTile + 16 * m + 8 * hf));
         r1acc[u] = mfma_bf16(zth[m], xb, r1acc[u]);
         r1acc[u] = mfma_bf16(ztl[m], xb, r1acc[u]);
       }
     }
+    // xbar rows of the block: 16-byte chunks
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = lane + 64 * i;
+      const int tok = q / (WC / 8);
+      const int cc = (q % (WC / 8)) * 8;
+      const u32x4 v = *(const u32x4*)(ys + tok * WC + cc);
+      if (n0 + tok < a.N && cc < ncol) *(u32x4*)(a.xbar + (n0 + tok) * a.h + c0 + cc) = v;
+    }
+  };
+  Blk b0, b1;
+  const long long st = a.slotsX, last = a.NB - 1;
+  long long j = s;
+  load_blk(j, b0);
+  for (;; j += 2 * st) {
+    load_blk(j + st < last ? j + st : last, b1);
+    work(j, b0);
+    if (j + st >= a.NB) break;
+    load_blk(j + 2 * st < last ? j + 2 * st : last, b0);
+    work(j + st, b1);
+    if (j + 2 * st >= a.NB) break;
   }
   // partial rows [slot][h][32]: rank 8(v/4) + 4hf + v%4 of column h
 #pragma unroll
   for (int u = 0; u < HT; ++u) {
-    if (ht0 + u >= nht) break;
-    const int hc = (ht0 + u) * kTile + col;
+    if (u * kTile >= ncol) break;
+    const int hc = c0 + u * kTile + col;
     float* dst = a.r1part + ((size_t)s * a.h + hc) * kBwdRow + 4 * hf;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -445,7 +537,10 @@ static hipError_t launch_r(const BwdArgs& a, size_t tok_lds, int cus, hipStream_
   const long long tg = std::max<long long>(1, std::min<long long>(cus, ((long long)a.NB + kBwdTokWaves - 1) / kBwdTokWaves));
   hipLaunchKernelGGL(bwd_tok_kernel<R16>, dim3((unsigned)tg), dim3(64 * kBwdTokWaves), tok_lds, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_exp_kernel<R16>, dim3((unsigned)(a.slotsE * a.GE)), dim3(64 * kBwdExpWaves), 0, stream, a);
+  if (a.k <= 8)
+    hipLaunchKernelGGL((bwd_exp_kernel<R16, 4>), dim3((unsigned)(a.slotsE * a.GE)), dim3(64 * kBwdExpWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_exp_kernel<R16, 16>), dim3((unsigned)(a.slotsE * a.GE)), dim3(64 * kBwdExpWaves), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_x_kernel<R16>, dim3((unsigned)(a.slotsX * a.GX)), dim3(64 * kBwdXWaves), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -25,7 +25,7 @@
 //                    part adds tvbar times R2's selected columns.  Writes g,
 //                    zbar and z (fp32 rows of 32).
 //   bwd_exp_kernel   expert-stationary (lane = expert, as psum_kernel): each
-//                    wave keeps 8 tiles' operands and their R2bar partials
+//                    wave keeps 4 tiles' operands and their R2bar partials
 //                    (32 x 32 fp32 each) in registers, recomputes P for the
 //                    token blocks of its slot, adds tvbar through a per-wave
 //                    LDS tile, and accumulates R2bar += z^T ybar (MFMA) and
@@ -46,7 +46,7 @@ namespace more {
 constexpr int kBwdSlots = 64;      // token slots of the expert- and h-stationary kernels
 constexpr int kBwdTokWaves = 8;    // bwd_tok_kernel waves per workgroup
 constexpr int kBwdExpWaves = 4;    // bwd_exp_kernel: one wave per SIMD (register-heavy)
-constexpr int kBwdExpTiles = 8;    // expert tiles per bwd_exp wave
+constexpr int kBwdExpTiles = 4;    // expert tiles per bwd_exp wave
 constexpr int kBwdXWaves = 4;
 constexpr int kBwdXTiles = 4;      // h tiles (32 columns) per bwd_x wave
 constexpr int kBwdRow = 32;        // row stride of z, zbar (ranks padded to 32)
@@ -72,6 +72,7 @@ struct BwdArgs {
   uint16_t* R2t;            // [M][32]
   int* invpos;              // [M]
   // intermediates
+  int* selpos;              // N x k: sweep position * 32 + token within its block
   float* g;                 // N
   float* zbar;              // N x 32
   float* zrm;               // N x 32

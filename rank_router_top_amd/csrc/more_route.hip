@@ -555,8 +555,8 @@ namespace {
 // Workspace of the backward call: packed weights, z scratch for N tokens,
 // then the backward's own area.
 struct BwdLayout {
-  size_t off_z, off_pbq, off_pbpos, off_r2b, off_r2t, off_inv, off_g, off_zbar, off_zrm, off_r2part, off_bpart,
-      off_r1part, total;
+  size_t off_z, off_pbq, off_pbpos, off_r2b, off_r2t, off_inv, off_sel, off_g, off_zbar, off_zrm, off_r2part,
+      off_bpart, off_r1part, total;
   int slotsE, slotsX, GE, GX;
 };
 bool backward_layout(more_dtype dt, const Layout& L, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k,
@@ -586,6 +586,8 @@ bool backward_layout(more_dtype dt, const Layout& L, int64_t N, int64_t h, int64
   off += align_up((size_t)M * kBwdRow * 2);
   B->off_inv = off;
   off += align_up((size_t)M * sizeof(int));
+  B->off_sel = off;
+  off += align_up((size_t)std::max<int64_t>(N, 1) * (size_t)k * sizeof(int));
   B->off_g = off;
   off += align_up(nrow * sizeof(float));
   B->off_zbar = off;
@@ -676,6 +678,7 @@ more_status more_lowrank_backward_packed(more_dtype dt, const void* X, int64_t N
   a.R2b = (uint16_t*)(ws + B.off_r2b);
   a.R2t = (uint16_t*)(ws + B.off_r2t);
   a.invpos = (int*)(ws + B.off_inv);
+  a.selpos = (int*)(ws + B.off_sel);
   a.g = (float*)(ws + B.off_g);
   a.zbar = (float*)(ws + B.off_zbar);
   a.zrm = (float*)(ws + B.off_zrm);

@@ -148,3 +148,29 @@ def test_dispatch_workspace_and_validation():
     assert f(FAKE, 10, 4, 64, FAKE, FAKE, FAKE, FAKE, 16, None) == 6
     assert f(FAKE, 0, 4, 64, None, None, None, None, 0, None) == 0            # N = 0: no-op
     assert f(FAKE, -1, 4, 64, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 2
+
+
+def call_backward(dt=0, N=64, h=256, r=32, M=4096, k=8, idx=FAKE, tv=FAKE, pb=None, lse=FAKE, xg=FAKE,
+                  r1g=FAKE, r2g=FAKE, bg=None, ws=FAKE, ws_bytes=100):
+    return R.lib().more_lowrank_backward_packed(dt, FAKE, N, h, FAKE, r, FAKE, M, k, idx, tv, pb, lse, xg, r1g, r2g,
+                                                bg, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(r=64), 7), (dict(r=128), 7), (dict(dt=1), 7), (dict(h=240), 7), (dict(M=20000), 7),
+    (dict(lse=None), 1), (dict(xg=None), 1), (dict(r1g=None), 1), (dict(r2g=None), 1), (dict(idx=None), 1),
+    (dict(tv=None), 1), (dict(xg=ODD), 9), (dict(pb=ODD), 9), (dict(k=33), 3), (dict(ws_bytes=100), 6),
+])
+def test_backward_rejects_bad_arguments_before_any_hip_call(kw, code):
+    assert call_backward(**kw) == code
+
+
+def test_backward_workspace_bytes():
+    bf = R.MORE_DT_BF16
+    assert R.backward_workspace_bytes(bf, 262144, 2048, 32, 4096, 8) > R.workspace_bytes(
+        False, bf, 262144, 2048, 32, 4096, 8, 0, True)
+    assert R.backward_workspace_bytes(bf, 100, 2048, 16, 4096, 32) > 0
+    assert R.backward_workspace_bytes(bf, 100, 2048, 64, 4096, 8) == 0      # r > 32
+    assert R.backward_workspace_bytes(bf, 100, 2048, 32, 16384, 8) > 0
+    assert R.backward_workspace_bytes(bf, 100, 2048, 32, 16385, 8) == 0     # M > 16384
+    assert R.backward_workspace_bytes(R.MORE_DT_F32, 100, 2048, 32, 4096, 8) == 0
