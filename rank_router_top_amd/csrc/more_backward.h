@@ -48,7 +48,7 @@ constexpr int kBwdTokWaves = 8;    // bwd_tok_kernel waves per workgroup
 constexpr int kBwdExpWaves = 4;    // bwd_exp_kernel: one wave per SIMD (register-heavy)
 constexpr int kBwdExpTiles = 4;    // expert tiles per bwd_exp wave
 constexpr int kBwdXWaves = 4;
-constexpr int kBwdXTiles = 4;      // h tiles (32 columns) per bwd_x wave
+constexpr int kBwdXTiles = 2;      // h tiles (32 columns) per bwd_x wave
 constexpr int kBwdRow = 32;        // row stride of z, zbar (ranks padded to 32)
 
 struct BwdArgs {
