@@ -163,12 +163,29 @@ __global__ __launch_bounds__(64 * kBwdTokWaves) void bwd_tok_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------- expert-stationary
+// Workgroup of kBwdExpWaves waves; wave w owns TW consecutive expert tiles.
+// All waves walk the same token blocks (s, s + slots, ...): the block's
+// operands (z in the B layout, lse, g, z rows, the selections) are staged once
+// in LDS by the whole workgroup, one block ahead (global loads issued before
+// the current block is swept, written to the other LDS buffer after it).
 template <int R16, int NS>
 __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
   constexpr int TW = kBwdExpTiles;
+  constexpr int NTH = 64 * kBwdExpWaves;
+  constexpr int ZB = 2 * R16 * 1024;              // z block bytes
+  constexpr int SELMAX = 64 * NS;                 // >= 32 k entries (NS = ceil(32 k / 64))
+  struct Buf {
+    u32x4 z[ZB / 16];
+    float lse[kTile], g[kTile];
+    float zr[kTile * kBwdRow];
+    int sp[SELMAX];
+    float sv[SELMAX];
+  };
+  __shared__ __align__(16) Buf buf[2];
   __shared__ __align__(16) float dt[kBwdExpWaves][kTile * kTile];   // per wave: ybar tile [expert col][token]
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = blockIdx.x / a.GE, gq = blockIdx.x % a.GE;
   const int t0 = (gq * kBwdExpWaves + wave) * TW;
   const int hf = lane >> 5, col = lane & 31;
@@ -196,77 +213,109 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
     for (int v = 0; v < 16; ++v) r2acc[u][v] = 0.f;
     bacc[u] = 0.f;
   }
-  // selections of a block per lane: 32 k / 64 <= NS
   const long long nk = a.N * a.k;
-  // loads of one token block (raw; masked where used)
-  struct Blk {
-    bf16x8 zh[R16], zl[R16];
-    float lr[16], gr[16], zt[16], sv[NS];
-    int sp[NS];
+  const int nsel = kTile * a.k;
+  // staging: each thread moves a fixed share of the block's operands
+  constexpr int ZCH = ZB / 16;                    // 16-byte chunks of z
+  constexpr int ZRC = kTile * kBwdRow / 4;        // float4 chunks of the z rows
+  struct Pre {
+    u32x4 z[(ZCH + NTH - 1) / NTH];
+    float4 zr[(ZRC + NTH - 1) / NTH];
+    float lse, g;
+    int sp[(SELMAX + NTH - 1) / NTH];
+    float sv[(SELMAX + NTH - 1) / NTH];
   };
-  auto load_blk = [&](long long j, Blk& B) {
+  auto fetch = [&](long long j, Pre& P) {
     const long long n0 = j * kTile;
-    const rsrc_t zd = make_rsrc((const char*)a.Z + (size_t)j * z_block_bytes(R16), z_block_bytes(R16));
+    const u32x4* zsrc = (const u32x4*)((const char*)a.Z + (size_t)j * z_block_bytes(R16));
+#pragma unroll
+    for (int i = 0; i < (ZCH + NTH - 1) / NTH; ++i) {
+      const int c = tid + NTH * i;
+      P.z[i] = zsrc[c < ZCH ? c : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < (ZRC + NTH - 1) / NTH; ++i) {
+      const int c = tid + NTH * i;
+      const long long row = n0 + (c < ZRC ? c : 0) / (kBwdRow / 4);
+      P.zr[i] = *(const float4*)(a.zrm + (row < a.N ? row : a.N - 1) * kBwdRow + 4 * ((c < ZRC ? c : 0) % (kBwdRow / 4)));
+    }
+    const long long tk = n0 + (tid & 31);
+    P.lse = a.lse[tk < a.N ? tk : a.N - 1];
+    P.g = a.g[tk < a.N ? tk : a.N - 1];
+#pragma unroll
+    for (int i = 0; i < (SELMAX + NTH - 1) / NTH; ++i) {
+      long long q = n0 * a.k + tid + NTH * i;
+      q = q < nk ? q : nk - 1;
+      P.sp[i] = a.selpos[q];
+      P.sv[i] = a.tv[q];
+    }
+  };
+  auto stage = [&](long long j, const Pre& P, Buf& B) {
+    const long long n0 = j * kTile;
+#pragma unroll
+    for (int i = 0; i < (ZCH + NTH - 1) / NTH; ++i) {
+      const int c = tid + NTH * i;
+      if (c < ZCH) B.z[c] = P.z[i];
+    }
+#pragma unroll
+    for (int i = 0; i < (ZRC + NTH - 1) / NTH; ++i) {
+      const int c = tid + NTH * i;
+      if (c < ZRC) {
+        const bool ok = n0 + c / (kBwdRow / 4) < a.N;
+        *(float4*)(B.zr + 4 * c) = ok ? P.zr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    if (tid < kTile) {
+      const bool ok = n0 + tid < a.N;
+      B.lse[tid] = ok ? -P.lse : -__builtin_inff();   // accumulator start: tokens past N give P = 0
+      B.g[tid] = P.g;
+    }
+#pragma unroll
+    for (int i = 0; i < (SELMAX + NTH - 1) / NTH; ++i) {
+      const int q = tid + NTH * i;
+      if (q < SELMAX) {
+        const bool ok = q < nsel && n0 + q / a.k < a.N;
+        B.sp[q] = ok ? P.sp[i] : -1;
+        B.sv[q] = P.sv[i];
+      }
+    }
+  };
+  auto work = [&](const Buf& B) {
+    bf16x8 zh[R16], zl[R16];
 #pragma unroll
     for (int m = 0; m < R16; ++m) {
-      B.zh[m] = buf_load(zd, lane * 16 + m * 1024, 0);
-      B.zl[m] = buf_load(zd, lane * 16 + (R16 + m) * 1024, 0);
+      zh[m] = __builtin_bit_cast(bf16x8, B.z[m * 64 + lane]);
+      zl[m] = __builtin_bit_cast(bf16x8, B.z[(R16 + m) * 64 + lane]);
     }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const long long tk = n0 + 8 * (v >> 2) + 4 * hf + (v & 3);
-      const long long tc = tk < a.N ? tk : a.N - 1;
-      B.lr[v] = a.lse[tc];
-      B.gr[v] = a.g[tc];
-      // z^T operand: K slot e' of step m = token 16m + 8(e'/4) + 4hf + e'%4, rank = col
-      const long long tz = n0 + 16 * (v >> 3) + 8 * ((v & 7) >> 2) + 4 * hf + (v & 3);
-      B.zt[v] = a.zrm[(tz < a.N ? tz : a.N - 1) * kBwdRow + col];
-    }
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      long long q = n0 * a.k + lane + 64 * i;
-      q = q < nk ? q : nk - 1;
-      B.sp[i] = a.selpos[q];
-      B.sv[i] = a.tv[q];
-    }
-  };
-  auto work = [&](long long j, const Blk& B) {
-    __builtin_amdgcn_sched_barrier(0);
-    const long long n0 = j * kTile;
     floatx16 c0;
     float gv[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const long long tk = n0 + 8 * (v >> 2) + 4 * hf + (v & 3);
-      c0[v] = tk < a.N ? -B.lr[v] : -__builtin_inff();
-      gv[v] = B.gr[v];
+    for (int q = 0; q < 4; ++q) {
+      const float4 l4 = *(const float4*)(B.lse + 8 * q + 4 * hf);
+      const float4 g4 = *(const float4*)(B.g + 8 * q + 4 * hf);
+      c0[4 * q] = l4.x; c0[4 * q + 1] = l4.y; c0[4 * q + 2] = l4.z; c0[4 * q + 3] = l4.w;
+      gv[4 * q] = g4.x; gv[4 * q + 1] = g4.y; gv[4 * q + 2] = g4.z; gv[4 * q + 3] = g4.w;
     }
+    // z^T operand: K slot e' of step m = token 16m + 8(e'/4) + 4hf + e'%4, rank = col
     bf16x8 zth[2], ztl[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const long long tz = n0 + 16 * m + 8 * (e >> 2) + 4 * hf + (e & 3);
-        x[e] = tz < a.N ? B.zt[8 * m + e] : 0.f;
-      }
+      for (int e = 0; e < 8; ++e) x[e] = B.zr[(16 * m + 8 * (e >> 2) + 4 * hf + (e & 3)) * kBwdRow + col];
       split8(x, zth[m], ztl[m]);
     }
     int spos[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int q = lane + 64 * i;
-      const bool ok = q < kTile * a.k && n0 + q / a.k < a.N;
-      spos[i] = ok ? B.sp[i] : -1;
-    }
+    for (int i = 0; i < NS; ++i) spos[i] = B.sp[lane + 64 * i];
 #pragma unroll
     for (int u = 0; u < TW; ++u) {
       const int t = t0 + u;
       floatx16 acc = c0;
 #pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(B.zh[m], w[u][m], acc);
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(zh[m], w[u][m], acc);
 #pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(B.zl[m], w[u][m], acc);
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(zl[m], w[u][m], acc);
       float d[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) d[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kLog2e, bl[u])) * (pb[u] - gv[v]);
@@ -280,7 +329,7 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
         for (int q = 0; q < 4; ++q) *(float4*)(row + 8 * q) = make_float4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
 #pragma unroll
         for (int i = 0; i < NS; ++i)
-          if (spos[i] >= 0 && (spos[i] >> 10) == t) my[((spos[i] >> 5) & 31) * kTile + (spos[i] & 31)] += B.sv[i];
+          if (spos[i] >= 0 && (spos[i] >> 10) == t) my[((spos[i] >> 5) & 31) * kTile + (spos[i] & 31)] += B.sv[lane + 64 * i];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 x = *(const float4*)(row + 8 * q);
@@ -304,17 +353,19 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
       }
     }
   };
-  Blk b0, b1;
-  const long long st = a.slotsE, last = a.NB - 1;
+  Pre P;
   long long j = s;
-  load_blk(j, b0);
-  for (;; j += 2 * st) {
-    load_blk(j + st < last ? j + st : last, b1);
-    work(j, b0);
-    if (j + st >= a.NB) break;
-    load_blk(j + 2 * st < last ? j + 2 * st : last, b0);
-    work(j + st, b1);
-    if (j + 2 * st >= a.NB) break;
+  fetch(j, P);
+  stage(j, P, buf[0]);
+  __syncthreads();
+  int cur = 0;
+  for (; j < a.NB; j += a.slotsE) {
+    const bool more = j + a.slotsE < a.NB;
+    if (more) fetch(j + a.slotsE, P);
+    work(buf[cur]);
+    if (more) stage(j + a.slotsE, P, buf[cur ^ 1]);
+    __syncthreads();   // next buffer complete; the current one is free again
+    cur ^= 1;
   }
   // partials: R2bar^T rows rho = 8(v/4) + 4hf + v%4, column = this lane's position
 #pragma unroll

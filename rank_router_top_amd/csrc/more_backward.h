@@ -25,9 +25,10 @@
 //                    part adds tvbar times R2's selected columns.  Writes g,
 //                    zbar and z (fp32 rows of 32).
 //   bwd_exp_kernel   expert-stationary (lane = expert, as psum_kernel): each
-//                    wave keeps 4 tiles' operands and their R2bar partials
-//                    (32 x 32 fp32 each) in registers, recomputes P for the
-//                    token blocks of its slot, adds tvbar through a per-wave
+//                    wave keeps 2 tiles' operands and their R2bar partials
+//                    (32 x 32 fp32 each) in registers; the workgroup stages
+//                    each token block's operands in LDS once, one block ahead;
+//                    each wave recomputes P, adds tvbar through a per-wave
 //                    LDS tile, and accumulates R2bar += z^T ybar (MFMA) and
 //                    bbar (in-lane sums).
 //   bwd_x_kernel     streams X once: per 32-token block and 32-column h tile,
@@ -45,8 +46,8 @@ namespace more {
 
 constexpr int kBwdSlots = 64;      // token slots of the expert- and h-stationary kernels
 constexpr int kBwdTokWaves = 8;    // bwd_tok_kernel waves per workgroup
-constexpr int kBwdExpWaves = 4;    // bwd_exp_kernel: one wave per SIMD (register-heavy)
-constexpr int kBwdExpTiles = 4;    // expert tiles per bwd_exp wave
+constexpr int kBwdExpWaves = 8;    // bwd_exp_kernel waves per workgroup (two per SIMD)
+constexpr int kBwdExpTiles = 2;    // expert tiles per bwd_exp wave
 constexpr int kBwdXWaves = 4;
 constexpr int kBwdXTiles = 2;      // h tiles (32 columns) per bwd_x wave
 constexpr int kBwdRow = 32;        // row stride of z, zbar (ranks padded to 32)
