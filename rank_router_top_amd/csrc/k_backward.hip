@@ -90,14 +90,15 @@ __global__ __launch_bounds__(64 * kBwdTokWaves) void bwd_tok_kernel(BwdArgs a) {
       return acc;
     };
     // sweep 1: g = sum over experts of pbar P (this lane's 16 rows, then both halves)
-    float gl = 0.f;
+    float gp[4] = {0.f, 0.f, 0.f, 0.f};
     load_w(0, wc);
     for (int t = 0; t < NT; ++t) {
       const floatx16 acc = logits(t);
       const floatx16 pq = *(const floatx16*)(lp + (2 * t + hf) * 16);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) gl += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kLog2e, nl)) * pq[v];
+      for (int v = 0; v < 16; ++v) gp[v & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kLog2e, nl)) * pq[v];
     }
+    const float gl = (gp[0] + gp[1]) + (gp[2] + gp[3]);
     const float g = gl + partner_f32(gl, hf != 0);
     if (ok && hf == 0) a.g[n] = g;
     // sweep 2: dense ybar -> zbar^T (rows rho, column = this token)
@@ -308,50 +309,68 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
     int spos[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) spos[i] = B.sp[lane + 64 * i];
+    // The TW tiles are processed phase by phase (logits, P and ybar, selected
+    // entries, MFMAs), so the dependent chains of different tiles interleave.
+    floatx16 acc[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) acc[u] = c0;
+#pragma unroll
+    for (int m = 0; m < R16; ++m)
+#pragma unroll
+      for (int u = 0; u < TW; ++u) acc[u] = mfma_bf16(zh[m], w[u][m], acc[u]);
+#pragma unroll
+    for (int m = 0; m < R16; ++m)
+#pragma unroll
+      for (int u = 0; u < TW; ++u) acc[u] = mfma_bf16(zl[m], w[u][m], acc[u]);
+    float d[TW][16];
+#pragma unroll
+    for (int u = 0; u < TW; ++u)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        d[u][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[u][v], kLog2e, bl[u])) * (pb[u] - gv[v]);
 #pragma unroll
     for (int u = 0; u < TW; ++u) {
-      const int t = t0 + u;
-      floatx16 acc = c0;
-#pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(zh[m], w[u][m], acc);
-#pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(zl[m], w[u][m], acc);
-      float d[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) d[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kLog2e, bl[u])) * (pb[u] - gv[v]);
       // selected (token, expert) pairs in this tile: add tvbar through the LDS tile
+      const int t = t0 + u;
       bool hit = false;
 #pragma unroll
       for (int i = 0; i < NS; ++i) hit = hit || (spos[i] >= 0 && (spos[i] >> 10) == t);
       if (any_lane(hit)) {
         float* row = my + col * kTile + 4 * hf;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *(float4*)(row + 8 * q) = make_float4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
+        for (int q = 0; q < 4; ++q)
+          *(float4*)(row + 8 * q) = make_float4(d[u][4 * q], d[u][4 * q + 1], d[u][4 * q + 2], d[u][4 * q + 3]);
 #pragma unroll
         for (int i = 0; i < NS; ++i)
           if (spos[i] >= 0 && (spos[i] >> 10) == t) my[((spos[i] >> 5) & 31) * kTile + (spos[i] & 31)] += B.sv[lane + 64 * i];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 x = *(const float4*)(row + 8 * q);
-          d[4 * q] = x.x;
-          d[4 * q + 1] = x.y;
-          d[4 * q + 2] = x.z;
-          d[4 * q + 3] = x.w;
+          d[u][4 * q] = x.x;
+          d[u][4 * q + 1] = x.y;
+          d[u][4 * q + 2] = x.z;
+          d[u][4 * q + 3] = x.w;
         }
       }
+    }
+    bf16x8 dh[TW][2], dl[TW][2];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
       float bs = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) bs += d[v];
+      for (int v = 0; v < 16; ++v) bs += d[u][v];
       bacc[u] += bs;
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        bf16x8 hi, lo;
-        split8(d + 8 * m, hi, lo);
-        r2acc[u] = mfma_bf16(zth[m], hi, r2acc[u]);
-        r2acc[u] = mfma_bf16(zth[m], lo, r2acc[u]);
-        r2acc[u] = mfma_bf16(ztl[m], hi, r2acc[u]);
-      }
+      for (int m = 0; m < 2; ++m) split8(d[u] + 8 * m, dh[u][m], dl[u][m]);
     }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int u = 0; u < TW; ++u) {
+        r2acc[u] = mfma_bf16(zth[m], dh[u][m], r2acc[u]);
+        r2acc[u] = mfma_bf16(zth[m], dl[u][m], r2acc[u]);
+        r2acc[u] = mfma_bf16(ztl[m], dh[u][m], r2acc[u]);
+      }
   };
   Pre P;
   long long j = s;
