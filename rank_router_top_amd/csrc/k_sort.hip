@@ -43,59 +43,36 @@ __global__ __launch_bounds__(kSortThreads) void sort_hist_kernel(SortPassArgs a)
   if (threadIdx.x < kSortBuckets) a.hist[(size_t)threadIdx.x * a.B + blockIdx.x] = h[threadIdx.x];
 }
 
-// One workgroup: in-place exclusive scan of the 64 * B counts, in chunks that
-// are staged in LDS with coalesced loads and stores.
-__global__ __launch_bounds__(kSortScanThreads) void sort_scan_kernel(int* hist, int total) {
-  constexpr int kPer = 16;
-  constexpr int kChunk = kSortScanThreads * kPer;
+// One workgroup per digit d: in-place exclusive scan of row d of the
+// (digit, block) counts, and the row total in tot[d].
+__global__ __launch_bounds__(kSortScanThreads) void sort_scan_kernel(int* hist, int* tot, int B) {
   constexpr int kWaves = kSortScanThreads / 64;
-  __shared__ int buf[kChunk];
   __shared__ int wsum[kWaves];
   __shared__ int carry_s;
+  const int d = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   if (threadIdx.x == 0) carry_s = 0;
-  for (int c0 = 0; c0 < total; c0 += kChunk) {
-    __syncthreads();
-    {
-      int t[kPer];   // all loads of the chunk in flight at once
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int i = c0 + j * kSortScanThreads + threadIdx.x;
-        t[j] = i < total ? hist[i] : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) buf[j * kSortScanThreads + threadIdx.x] = t[j];
-    }
-    __syncthreads();
-    // each thread scans its kPer consecutive entries
-    int v[kPer], s = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      v[j] = s;
-      s += buf[threadIdx.x * kPer + j];
-    }
-    // inclusive scan of the thread sums within the wave, then across waves
-    int x = s;
+  int* row = hist + (size_t)d * B;
+  for (int c0 = 0; c0 < B; c0 += kSortScanThreads) {
+    const int i = c0 + threadIdx.x;
+    const int v = i < B ? row[i] : 0;
+    int x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(x, o);
       if (lane >= o) x += y;
     }
+    __syncthreads();   // wsum and carry_s of the previous chunk have been read
     if (lane == 63) wsum[wv] = x;
     __syncthreads();
     int before = carry_s;
-    for (int i = 0; i < wv; ++i) before += wsum[i];
-    before += x - s;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) buf[threadIdx.x * kPer + j] = before + v[j];
+    for (int k = 0; k < wv; ++k) before += wsum[k];
+    if (i < B) row[i] = before + x - v;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = c0 + j * kSortScanThreads + threadIdx.x;
-      if (i < total) hist[i] = buf[j * kSortScanThreads + threadIdx.x];
-    }
-    if (threadIdx.x == kSortScanThreads - 1) carry_s = before + s;
+    if (threadIdx.x == kSortScanThreads - 1) carry_s = before + x;
   }
+  __syncthreads();
+  if (threadIdx.x == 0) tot[d] = carry_s;
 }
 
 __global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(SortPassArgs a) {
@@ -128,23 +105,61 @@ __global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(SortPassArgs
     if (ok && rank == 0) cnt[w][d] = old + __builtin_popcountll(peers);
   }
   __syncthreads();
-  // per digit: this block's base, then each wave's start after the waves before it
+  // per digit (one lane each of the first wave): the block's elements of
+  // digit d go to block-local positions bstart[d] + (waves before) + rank, and
+  // from there to the global start of (d, this block): the totals of the
+  // digits below plus this block's offset in row d
+  __shared__ int bstart[kSortBuckets], gbase[kSortBuckets];
   if (threadIdx.x < kSortBuckets) {
-    int run = a.hist[(size_t)threadIdx.x * a.B + blockIdx.x];
+    const int d = threadIdx.x;
+    const int tt = a.tot[d];
+    int bt = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) bt += cnt[i][d];
+    int x = tt, y = bt;
+#pragma unroll
+    for (int o = 1; o < kSortBuckets; o <<= 1) {
+      const int x2 = __shfl_up(x, o), y2 = __shfl_up(y, o);
+      if (d >= o) {
+        x += x2;
+        y += y2;
+      }
+    }
+    const int bs = y - bt;   // exclusive prefix of the block's digit counts
+    bstart[d] = bs;
+    gbase[d] = a.hist[(size_t)d * a.B + blockIdx.x] + x - tt;
+    int run = bs;
 #pragma unroll
     for (int i = 0; i < W; ++i) {
-      const int c = cnt[i][threadIdx.x];
-      cnt[i][threadIdx.x] = run;
+      const int c = cnt[i][d];
+      cnt[i][d] = run;
       run += c;
     }
   }
   __syncthreads();
+  // stage the block in LDS in its sorted order, then write it out with
+  // consecutive lanes on consecutive positions of each digit's run
+  __shared__ int ks[kSortBlock], vs[kSortBlock];
 #pragma unroll
   for (int r = 0; r < kSortRounds; ++r) {
     if (e0 + r * 64 < a.n) {
       const int p = cnt[w][sort_digit(key[r], a.shift)] + pos[r];
-      a.keys_out[p] = key[r];
-      a.vals_out[p] = val[r];
+      ks[p] = key[r];
+      vs[p] = val[r];
+    }
+  }
+  __syncthreads();
+  const long long b0 = (long long)blockIdx.x * kSortBlock;
+  const int nvalid = a.n - b0 < kSortBlock ? (int)(a.n - b0) : kSortBlock;
+#pragma unroll
+  for (int r = 0; r < kSortRounds; ++r) {
+    const int i = threadIdx.x + kSortThreads * r;
+    if (i < nvalid) {
+      const int k = ks[i];
+      const int d = sort_digit(k, a.shift);
+      const int p = gbase[d] + (i - bstart[d]);
+      a.keys_out[p] = k;
+      a.vals_out[p] = vs[i];
     }
   }
 }
@@ -176,11 +191,12 @@ hipError_t launch_dispatch_sort(const int* idx, int n, int M, int* sorted_expert
     a.keys_out = to_out ? sorted_expert : tmp_keys;
     a.vals_out = to_out ? sorted_slot : tmp_vals;
     a.hist = hist;
+    a.tot = hist + (size_t)kSortBuckets * B;
     a.n = n;
     a.B = B;
     a.shift = p * kSortDigitBits;
     hipLaunchKernelGGL(sort_hist_kernel, dim3((unsigned)B), dim3(kSortThreads), 0, stream, a);
-    hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(kSortScanThreads), 0, stream, hist, kSortBuckets * B);
+    hipLaunchKernelGGL(sort_scan_kernel, dim3(kSortBuckets), dim3(kSortScanThreads), 0, stream, hist, hist + (size_t)kSortBuckets * B, B);
     hipLaunchKernelGGL(sort_scatter_kernel, dim3((unsigned)B), dim3(kSortThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -709,7 +709,7 @@ size_t more_dispatch_workspace_bytes(int64_t N, int32_t k, int64_t M) {
     return 0;
   const int64_t n = N * k;
   const int64_t B = (n + kSortBlock - 1) / kSortBlock;
-  size_t bytes = align_up((size_t)(B > 0 ? B : 1) * kSortBuckets * sizeof(int));
+  size_t bytes = align_up(((size_t)(B > 0 ? B : 1) + 1) * kSortBuckets * sizeof(int));
   if (sort_passes(M) > 1) bytes += 2 * align_up((size_t)(n > 0 ? n : 1) * sizeof(int));
   return bytes;
 }
@@ -733,7 +733,7 @@ more_status more_dispatch_sort(const int32_t* topk_idx, int64_t N, int32_t k, in
   int* tk = nullptr;
   int* tv = nullptr;
   if (sort_passes(M) > 1) {
-    const size_t off = align_up((size_t)B * kSortBuckets * sizeof(int));
+    const size_t off = align_up(((size_t)B + 1) * kSortBuckets * sizeof(int));
     tk = (int*)(ws + off);
     tv = (int*)(ws + off + align_up((size_t)n * sizeof(int)));
   }

@@ -12,9 +12,10 @@
 //   sort_hist_kernel     per-block digit histogram (64 bins; one LDS atomic
 //                        per group of equal digits in a wave round),
 //                        written digit-major: hist[d * B + b];
-//   sort_scan_kernel     one workgroup: exclusive scan of hist in (d, b)
-//                        order, staged through LDS -> the first output
-//                        position of digit d's elements from block b;
+//   sort_scan_kernel     one workgroup per digit: exclusive scan of row d of
+//                        hist and its total; the scatter adds the totals of
+//                        the digits below -> the first output position of
+//                        digit d's elements from block b;
 //   sort_scatter_kernel  the block's elements are ranked stably within the
 //                        block with wave ballots (a 64-way multisplit: six
 //                        ballots give each lane the mask of lanes with its
@@ -51,6 +52,7 @@ struct SortPassArgs {
   int* keys_out;
   int* vals_out;
   int* hist;            // [64][B]
+  const int* tot;       // [64] row totals of hist
   int n, B, shift;
 };
 
@@ -62,7 +64,7 @@ struct SortOffsetsArgs {
 
 // Enqueues every kernel of the sort on `stream`: passes P over (idx ->
 // ... -> sorted_expert, sorted_slot) with tmp_keys / tmp_vals between passes,
-// then the offsets.
+// then the offsets.  hist holds 64 B + 64 ints (counts, then row totals).
 hipError_t launch_dispatch_sort(const int* idx, int n, int M, int* sorted_expert, int* sorted_slot,
                                 int* offsets, int* hist, int* tmp_keys, int* tmp_vals, hipStream_t stream);
 

@@ -135,10 +135,11 @@ def test_balance_workspace_bytes():
 
 
 def test_dispatch_workspace_and_validation():
-    """Digit counts (64 per block of 4096 entries, 256-byte aligned) and, for
-    more than one radix pass (M > 64), a key and a slot buffer of N k entries."""
-    assert R.dispatch_workspace_bytes(262144, 8, 4096) == 512 * 64 * 4 + 2 * 262144 * 8 * 4
-    assert R.dispatch_workspace_bytes(1000, 4, 64) == 256
+    """Digit counts (64 per block of 4096 entries, plus 64 row totals, 256-byte
+    aligned) and, for more than one radix pass (M > 64), a key and a slot
+    buffer of N k entries."""
+    assert R.dispatch_workspace_bytes(262144, 8, 4096) == 513 * 64 * 4 + 2 * 262144 * 8 * 4
+    assert R.dispatch_workspace_bytes(1000, 4, 64) == 512
     assert R.dispatch_workspace_bytes(1000, 5, 4) == 0          # k > M
     assert R.dispatch_workspace_bytes(1 << 28, 8, 4096) == 0     # N k >= 2^31 - 1
     f = R.lib().more_dispatch_sort
