@@ -227,3 +227,19 @@ def test_balance_full_size_headline(oracle_lib):
     ob = dict(o, psum=ps_o)
     check_stats(ob, g, N, cfg.k, diff, "full-size")
     say(f"full size: ok {res} count moves {diff}")
+
+
+@pytest.mark.parametrize("spread", [30.0, 90.0])
+def test_balance_wide_bias_spread(oracle_lib, spread):
+    """Biases spread over +-spread/2 (natural log units): at 90 the spread of
+    a wave's experts exceeds the range where the psum sweep factors the bias
+    out of the exponentials (100 log2 units), so that wave takes the
+    unfactored form; both must match the oracle."""
+    N, h, r, M, k = 500, 256, 32, 4096, 8
+    X = I.make_x(5, 42, N, h, I.DT_BF16, True)
+    R1 = I.make_r1(5, 42, h, r, I.DT_BF16)
+    R2 = I.make_r2(5, 42, r, M, I.DT_BF16)
+    rng = np.random.default_rng(17)
+    b = (rng.uniform(-0.5, 0.5, M) * spread).astype(np.float32)
+    for gate in (CF.GATE_TOPK_SOFTMAX, CF.GATE_FULL_SOFTMAX):
+        check_balance(oracle_lib, X, R1, R2, b, k, gate, f"bias-spread-{spread:g}")
