@@ -50,10 +50,10 @@ __global__ __launch_bounds__(64 * kBwdTokWaves) void bwd_tok_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NT = a.NT;
-  float* lb = (float*)bt_lds;              // bias, accumulator layout
+  float* lb = (float*)bt_lds;              // bias * log2 e, accumulator layout
   float* lp = lb + NT * 32;                // pbar, accumulator layout
   for (int i = threadIdx.x; i < NT * 32; i += 64 * kBwdTokWaves) {
-    lb[i] = a.biasp[i];
+    lb[i] = a.biasp[i] * kLog2e;
     lp[i] = a.pbq[i];
   }
   __syncthreads();
@@ -71,7 +71,34 @@ __global__ __launch_bounds__(64 * kBwdTokWaves) void bwd_tok_kernel(BwdArgs a) {
       zh[m] = buf_load(zd, lane * 16 + m * 1024, 0);
       zl[m] = buf_load(zd, lane * 16 + (R16 + m) * 1024, 0);
     }
-    const float nl = ok ? -a.lse[n] * kLog2e : -__builtin_inff();
+    // The logits come out in log2 units and already shifted by -lse: z enters
+    // scaled by log2 e (hi + lo again), the bias from LDS is scaled, and one
+    // more MFMA adds -lse log2 e of each token (B operand: its hi and lo in K
+    // slots 0 and 1 of the token's lane; A operand: ones in those slots), so
+    // P = exp2(acc) with no per-logit VALU work.  Tokens past N get -1e30.
+    bf16x8 sh[R16], sl[R16];
+#pragma unroll
+    for (int m = 0; m < R16; ++m)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = ((float)zh[m][e] + (float)zl[m][e]) * kLog2e;
+        sh[m][e] = (bf16)x;
+        sl[m][e] = (bf16)(x - (float)sh[m][e]);
+      }
+    const float nl = ok ? -a.lse[n] * kLog2e : -1e30f;
+    bf16x8 one, shift;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      one[e] = (bf16)0.f;
+      shift[e] = (bf16)0.f;
+    }
+    if (hf == 0) {
+      one[0] = (bf16)1.f;
+      one[1] = (bf16)1.f;
+      const bf16 nh = (bf16)nl;
+      shift[0] = nh;
+      shift[1] = (bf16)(nl - (float)nh);
+    }
     // weight operands of tile t + 1 are requested before tile t is computed
     bf16x8 wc[R16], wn[R16];
     auto load_w = [&](int t, bf16x8 (&w)[R16]) {
@@ -82,9 +109,10 @@ __global__ __launch_bounds__(64 * kBwdTokWaves) void bwd_tok_kernel(BwdArgs a) {
       load_w(t + 1 < NT ? t + 1 : t, wn);
       floatx16 acc = *(const floatx16*)(lb + (2 * t + hf) * 16);
 #pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(wc[m], zh[m], acc);
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(wc[m], sh[m], acc);
 #pragma unroll
-      for (int m = 0; m < R16; ++m) acc = mfma_bf16(wc[m], zl[m], acc);
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(wc[m], sl[m], acc);
+      acc = mfma_bf16(one, shift, acc);
 #pragma unroll
       for (int m = 0; m < R16; ++m) wc[m] = wn[m];
       return acc;
@@ -96,7 +124,7 @@ __global__ __launch_bounds__(64 * kBwdTokWaves) void bwd_tok_kernel(BwdArgs a) {
       const floatx16 acc = logits(t);
       const floatx16 pq = *(const floatx16*)(lp + (2 * t + hf) * 16);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) gp[v & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kLog2e, nl)) * pq[v];
+      for (int v = 0; v < 16; ++v) gp[v & 3] += __builtin_amdgcn_exp2f(acc[v]) * pq[v];
     }
     const float gl = (gp[0] + gp[1]) + (gp[2] + gp[3]);
     const float g = gl + partner_f32(gl, hf != 0);
@@ -117,7 +145,7 @@ __global__ __launch_bounds__(64 * kBwdTokWaves) void bwd_tok_kernel(BwdArgs a) {
       const floatx16 pq = *(const floatx16*)(lp + (2 * t + hf) * 16);
       float d[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) d[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kLog2e, nl)) * (pq[v] - g);
+      for (int v = 0; v < 16; ++v) d[v] = __builtin_amdgcn_exp2f(acc[v]) * (pq[v] - g);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         bf16x8 hi, lo;
