@@ -211,7 +211,7 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
     float sv[SELMAX];
   };
   __shared__ __align__(16) Buf buf[2];
-  __shared__ __align__(16) float dt[kBwdExpWaves][kTile * kTile];   // per wave: ybar tile [expert col][token]
+  __shared__ __align__(16) float dt[kBwdExpWaves][TW * kTile * kTile];   // per wave: tvbar of its tiles [tile][expert col][token]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -222,7 +222,12 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
   float* my = dt[wave];
   const rsrc_t r2d = make_rsrc(a.R2p, a.NT * R16 * 1024);
   bf16x8 w[TW][R16];
-  float bl[TW], pb[TW];
+  float pb[TW];
+  // the bias of the lane's expert (log2 units) enters with one MFMA per tile:
+  // B operand bias hi, lo in K slots 0 and 1, A operand ones there
+  bf16x8 bo[TW], one;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) one[e] = (bf16)((hf == 0 && e < 2) ? 1.f : 0.f);
   {
     const int bidx = ((col >> 2) & 1) * 16 + 4 * (col >> 3) + (col & 3);
 #pragma unroll
@@ -230,8 +235,15 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
       const int t = t0 + u < a.NT ? t0 + u : a.NT - 1;
 #pragma unroll
       for (int m = 0; m < R16; ++m) w[u][m] = buf_load(r2d, lane * 16 + m * 1024, t * R16 * 1024);
-      bl[u] = a.biasp[t * 32 + bidx] * kLog2e;
+      const float bv = a.biasp[t * 32 + bidx];
+      const float b2 = bv > -__builtin_inff() ? bv * kLog2e : -1e30f;   // padding rows: P = 0
       pb[u] = a.pbpos[t * 32 + col];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bo[u][e] = (bf16)0.f;
+      if (hf == 0) {
+        bo[u][0] = (bf16)b2;
+        bo[u][1] = (bf16)(b2 - (float)bo[u][0]);
+      }
     }
   }
   floatx16 r2acc[TW];
@@ -248,7 +260,7 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
   constexpr int ZCH = ZB / 16;                    // 16-byte chunks of z
   constexpr int ZRC = kTile * kBwdRow / 4;        // float4 chunks of the z rows
   struct Pre {
-    u32x4 z[(ZCH + NTH - 1) / NTH];
+    u32x4 z[(ZCH + NTH - 1) / NTH], zl[(ZCH + NTH - 1) / NTH];   // hi chunk c and lo chunk c
     float4 zr[(ZRC + NTH - 1) / NTH];
     float lse, g;
     int sp[(SELMAX + NTH - 1) / NTH];
@@ -260,7 +272,8 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < (ZCH + NTH - 1) / NTH; ++i) {
       const int c = tid + NTH * i;
-      P.z[i] = zsrc[c < ZCH ? c : 0];
+      P.z[i] = zsrc[c < ZCH / 2 ? c : 0];
+      P.zl[i] = zsrc[ZCH / 2 + (c < ZCH / 2 ? c : 0)];
     }
 #pragma unroll
     for (int i = 0; i < (ZRC + NTH - 1) / NTH; ++i) {
@@ -281,10 +294,23 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
   };
   auto stage = [&](long long j, const Pre& P, Buf& B) {
     const long long n0 = j * kTile;
+    // z scaled by log2 e (hi + lo again): the logits come out in log2 units
 #pragma unroll
     for (int i = 0; i < (ZCH + NTH - 1) / NTH; ++i) {
       const int c = tid + NTH * i;
-      if (c < ZCH) B.z[c] = P.z[i];
+      if (c < ZCH / 2) {
+        const bf16x8 hv = __builtin_bit_cast(bf16x8, P.z[i]);
+        const bf16x8 lv = __builtin_bit_cast(bf16x8, P.zl[i]);
+        bf16x8 h2, l2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = ((float)hv[e] + (float)lv[e]) * kLog2e;
+          h2[e] = (bf16)x;
+          l2[e] = (bf16)(x - (float)h2[e]);
+        }
+        B.z[c] = __builtin_bit_cast(u32x4, h2);
+        B.z[ZCH / 2 + c] = __builtin_bit_cast(u32x4, l2);
+      }
     }
 #pragma unroll
     for (int i = 0; i < (ZRC + NTH - 1) / NTH; ++i) {
@@ -296,7 +322,7 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
     }
     if (tid < kTile) {
       const bool ok = n0 + tid < a.N;
-      B.lse[tid] = ok ? -P.lse : -__builtin_inff();   // accumulator start: tokens past N give P = 0
+      B.lse[tid] = ok ? -P.lse * kLog2e : -__builtin_inff();   // accumulator start: tokens past N give P = 0
       B.g[tid] = P.g;
     }
 #pragma unroll
@@ -350,35 +376,33 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
     for (int m = 0; m < R16; ++m)
 #pragma unroll
       for (int u = 0; u < TW; ++u) acc[u] = mfma_bf16(zl[m], w[u][m], acc[u]);
+#pragma unroll
+    for (int u = 0; u < TW; ++u) acc[u] = mfma_bf16(one, bo[u], acc[u]);
     float d[TW][16];
 #pragma unroll
     for (int u = 0; u < TW; ++u)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        d[u][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[u][v], kLog2e, bl[u])) * (pb[u] - gv[v]);
+      for (int v = 0; v < 16; ++v) d[u][v] = __builtin_amdgcn_exp2f(acc[u][v]) * (pb[u] - gv[v]);
+    // the block's tvbar in the wave's tiles, dense in LDS: cleared, scattered
+    // (a token selects an expert at most once), then read like ybar itself
+#pragma unroll
+    for (int i = 0; i < TW * kTile * kTile / 4 / 64; ++i)
+      *(float4*)(my + 4 * (lane + 64 * i)) = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int tl = (spos[i] >> 10) - t0;
+      if (spos[i] >= 0 && tl >= 0 && tl < TW) my[tl * kTile * kTile + (spos[i] & 1023)] = B.sv[lane + 64 * i];
+    }
 #pragma unroll
     for (int u = 0; u < TW; ++u) {
-      // selected (token, expert) pairs in this tile: add tvbar through the LDS tile
-      const int t = t0 + u;
-      bool hit = false;
+      const float* row = my + u * kTile * kTile + col * kTile + 4 * hf;
 #pragma unroll
-      for (int i = 0; i < NS; ++i) hit = hit || (spos[i] >= 0 && (spos[i] >> 10) == t);
-      if (any_lane(hit)) {
-        float* row = my + col * kTile + 4 * hf;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *(float4*)(row + 8 * q) = make_float4(d[u][4 * q], d[u][4 * q + 1], d[u][4 * q + 2], d[u][4 * q + 3]);
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-          if (spos[i] >= 0 && (spos[i] >> 10) == t) my[((spos[i] >> 5) & 31) * kTile + (spos[i] & 31)] += B.sv[lane + 64 * i];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 x = *(const float4*)(row + 8 * q);
-          d[u][4 * q] = x.x;
-          d[u][4 * q + 1] = x.y;
-          d[u][4 * q + 2] = x.z;
-          d[u][4 * q + 3] = x.w;
-        }
+      for (int q = 0; q < 4; ++q) {
+        const float4 x = *(const float4*)(row + 8 * q);
+        d[u][4 * q] += x.x;
+        d[u][4 * q + 1] += x.y;
+        d[u][4 * q + 2] += x.z;
+        d[u][4 * q + 3] += x.w;
       }
     }
     bf16x8 dh[TW][2], dl[TW][2];
