@@ -92,13 +92,15 @@ def parse():
 
 
 def source_hash():
-    """Hash of the HIP sources the library is built from: traffic counters taken
-    on another version of the kernels are not reported."""
+    """Hash of the HIP sources the routing call is built from: traffic counters
+    taken on another version of its kernels are not reported.  The files that
+    hold only the balancing, dispatch and backward kernels are left out."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_router_top_amd", "csrc")
+    other = {"k_backward.hip", "more_backward.h", "k_balance.hip", "more_balance.h", "k_sort.hip", "more_sort.h"}
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".h", ".hip")):
+        if name.endswith((".h", ".hip")) and name not in other:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
