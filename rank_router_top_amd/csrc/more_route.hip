@@ -19,6 +19,7 @@
 #include "more_device.h"
 #include "more_pack.h"
 #include "more_dispatch.h"
+#include "more_fullrank_tiled.h"
 #include "more_balance.h"
 #include "more_sort.h"
 #include "more_backward.h"
@@ -293,6 +294,8 @@ size_t more_route_workspace_bytes(int fullrank, more_dtype dt, int64_t N, int64_
   Layout L;
   make_layout(fullrank, dt, h, r, M, &L);
   if (N < 0) return 0;
+  if (fullrank && dt == MORE_DT_BF16 && fr_tiled_supported(h, M, k))
+    return std::max(L.total, align_up(fr_tiled_bytes(h, M)));
   return L.total + (fullrank ? 0 : z_scratch_bytes(dt, L, N));
 }
 
@@ -750,9 +753,17 @@ more_status more_route_fullrank(more_dtype dt, const void* X, int64_t N, int64_t
   if (st != MORE_OK || N == 0) return st;
   Layout L;
   make_layout(1, dt, h, 0, M, &L);
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == MORE_DT_BF16 && fr_tiled_supported(h, M, k)) {
+    // LDS-tiled MFMA sweep (k <= 8, h a multiple of 64)
+    if (!workspace || workspace_bytes < fr_tiled_bytes(h, M) || ((uintptr_t)workspace % kAlign) != 0)
+      return MORE_ERR_WORKSPACE;
+    return launch_fullrank_tiled((const uint16_t*)X, N, (int)h, (const uint16_t*)W, (int)M, bias, k,
+                                 gate == MORE_GATE_FULL_SOFTMAX, topk_idx, topk_gate, topk_logit, lse, workspace,
+                                 s) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+  }
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace % kAlign) != 0)
     return MORE_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   st = launch_pack(dt, 1, W, nullptr, bias, h, 0, M, L, ws, s);
   if (st != MORE_OK) return st;
