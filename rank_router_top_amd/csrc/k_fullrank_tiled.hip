@@ -12,14 +12,56 @@ constexpr int kFrThreads = 64 * kFrWaves;
 constexpr int kFrXBytes = kFrTokens * kFrChunk * 2;        // X chunk of the block
 constexpr int kFrWBytes = kFrSlab * kFrChunk * 2;          // weight chunk of the slab
 constexpr int kFrBBytes = kFrSlab * 4;                     // the slab's bias
-constexpr int kFrBuf = kFrXBytes + kFrWBytes + kFrBBytes;  // one LDS buffer
+constexpr int kFrWBuf = kFrWBytes + 2 * kFrBBytes;         // one weight + bias buffer (bias twice: see issue_w)
 constexpr int kFrUnitsW = kFrWBytes / 16;                  // 16-byte units of a weight chunk
-constexpr int kFrLists = 2 * (kFrWaves / 2);               // lists per token: 4 expert quarters x 2 halves
-static_assert(kFrThreads == kFrTokens * kFrChunk * 2 / 16, "one 16-byte X unit per thread");
+constexpr int kFrTiles = kFrSlab / 32;                     // 32-expert tiles of a slab
+constexpr int kFrLists = 2 * 2;                            // lists per token: 2 expert halves x 2 lane halves
+// Weight chunks are loaded 2 chunks ahead (3 buffers); X chunks, which miss
+// L2 (every slab re-reads the block), 5 chunks ahead (6 buffers).
+constexpr int kFrWBufs = 3;
+constexpr int kFrXBufs = 6;
+constexpr int kFrLds = kFrWBufs * kFrWBuf + kFrXBufs * kFrXBytes;
+static_assert(kFrLds <= 160 * 1024, "LDS of one workgroup");
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): wait until at most 5 / 3 / 0 vector-memory operations
+// of this wave are outstanding, nothing else.  Per chunk a lane issues 2 X
+// loads and 3 weight + bias loads.
+constexpr int kVmcnt5 = 0x0f70 | 5;
+constexpr int kVmcnt3 = 0x0f70 | 3;
+constexpr int kVmcnt0 = 0x0f70;
+static_assert(kFrTokens * kFrChunk * 2 == kFrWaves * 2 * kWave * 16, "two X operand blocks per wave");
 static_assert(kFrUnitsW % kFrThreads == 0, "whole weight units per thread");
-static_assert(kFrSlab == kFrThreads, "one bias value per thread");
-static_assert(kFrTokens * kFrLists * (kFrKmax + 1) * 8 <= 2 * kFrBuf, "merge area fits the operand buffers");
+static_assert(kFrSlab == 4 * kWave && kFrWaves == 8, "waves 0-3 load the bias, 4-7 a copy");
+static_assert(kFrTokens * kFrLists * (kFrKmax + 1) * 8 <= kFrLds, "merge area fits the operand buffers");
+static_assert(kFrTokens == kFrWaves * 32 && kFrSlab == 2 * 4 * 32, "wave (w % 4, w / 4): 2 token groups x 4 tiles");
 }  // namespace
+
+// Global -> LDS load of `bytes` (16 or 4) per lane: lane l's bytes land at
+// LDS byte address lds + l * bytes (lds wave-uniform, through M0).  Written as
+// inline assembly so that the compiler does not order LDS reads of the other
+// buffers behind it (it cannot tell the buffers apart and would wait for every
+// load in flight); the kernel waits for these loads itself (s_waitcnt vmcnt)
+// before the barrier that publishes a chunk.  No register is written.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; it is named to state that it changes
+__device__ __forceinline__ void fr_dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void fr_dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Publish a chunk: wait for this wave's loads of it (VMCNT_IMM lets the loads
+// of the next chunk stay in flight), then the workgroup barrier.  The empty asm
+// statements keep the compiler from moving LDS accesses across the barrier.
+template <int VMCNT_IMM>
+__device__ __forceinline__ void fr_publish() {
+  __builtin_amdgcn_s_waitcnt(VMCNT_IMM);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // One thread per 16-byte unit of packed weights; the first nslab * 512 threads
 // also write the bias in accumulator layout (lane half hf, register v holds
@@ -31,7 +73,7 @@ __global__ __launch_bounds__(256) void fr_pack_kernel(const uint16_t* __restrict
   const long long units = (long long)nslab * NC * kFrUnitsW;
   const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
   if (u < units) {
-    const int lane = (int)(u % 64), s = (int)((u / 64) % 2), t = (int)((u / 128) % 16);
+    const int lane = (int)(u % 64), s = (int)((u / 64) % 2), t = (int)((u / 128) % kFrTiles);
     const long long c = (u / kFrUnitsW) % NC, slab = u / (kFrUnitsW * NC);
     const long long j = slab * kFrSlab + t * 32 + (lane & 31);
     const long long k0 = c * kFrChunk + 16 * s + 8 * (lane >> 5);
@@ -45,7 +87,7 @@ __global__ __launch_bounds__(256) void fr_pack_kernel(const uint16_t* __restrict
     *(uint4*)(Wq + u * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   if (u < (long long)nslab * kFrSlab) {
-    const int v = (int)(u % 16), hf = (int)((u / 16) % 2), t = (int)((u / 32) % 16);
+    const int v = (int)(u % 16), hf = (int)((u / 16) % 2), t = (int)((u / 32) % kFrTiles);
     const long long slab = u / kFrSlab;
     const long long j = slab * kFrSlab + t * 32 + 8 * (v / 4) + 4 * hf + v % 4;
     biasq[u] = j < M ? (bias ? bias[j] : 0.f) : -__builtin_inff();
@@ -108,50 +150,45 @@ __device__ __forceinline__ void fr_fold(float (&T)[K], int (&P)[K], float& m, fl
 template <bool FULL>
 __global__ __launch_bounds__(kFrThreads) void fr_tiled_kernel(FrTiledArgs a) {
   constexpr int K = kFrKmax;
-  __shared__ __align__(16) char smem[2 * kFrBuf];
+  __shared__ __align__(16) char smem[kFrLds];   // [3 weight + bias buffers][6 X buffers]
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wt = w & 1, we = w >> 1;
+  const int wt = w & 3, we = w >> 2;
   const bool hi = lane >= 32;
   const int hf = hi ? 1 : 0, col = lane & 31;
   const long long tb0 = (long long)blockIdx.x * kFrTokens;
   const int NC = a.h / kFrChunk;   // even: h is a multiple of 2 kFrChunk
   const int Q = a.nslab * NC;
 
-  // staging: thread tid moves 16 bytes of token xt's 64-byte chunk row (part
-  // xq = K-step xq / 2, half xq % 2) and 64 bytes of the weight chunk
-  const int xt = tid >> 2, xq = tid & 3;
-  const long long xrow = tb0 + xt;
-  const bool xok = xrow < a.N;
-  const uint16_t* xsrc = a.X + (xok ? xrow : a.N - 1) * (long long)a.h + 8 * xq;
-  const int xdst = (((xt >> 5) * 2 + (xq >> 1)) * kWave + (xt & 31) + 32 * (xq & 1)) * 16;
-
-  struct Ld {
-    u32x4 x;
-    u32x4 w[kFrUnitsW / kFrThreads];
-    float b;
+  // Loads go straight from global memory into LDS (16 bytes per lane; the
+  // destination of a wave's load is 64 consecutive 16-byte slots): wave w
+  // fills the X operand blocks (group w, K-steps 0 and 1) of the chunk, two
+  // 1 KiB runs of the weight chunk and 64 bias values (waves 4-7 load a copy,
+  // so that every wave issues the same loads).  Rows past N read row N - 1:
+  // their logits are never stored.
+  const long long xrow = tb0 + w * kTile + col;
+  const uint16_t* xsrc = a.X + (xrow < a.N ? xrow : a.N - 1) * (long long)a.h + 8 * hf;
+  const uint32_t smem0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  auto issue_x = [&](int q) {
+    const int c = q % NC;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(smem0 + (uint32_t)(kFrWBufs * kFrWBuf + (q % kFrXBufs) * kFrXBytes));
+    fr_dma16(xsrc + (long long)c * kFrChunk, base + (2 * w + 0) * kWave * 16);
+    fr_dma16(xsrc + (long long)c * kFrChunk + 16, base + (2 * w + 1) * kWave * 16);
   };
-  auto fetch = [&](int q, Ld& L) {
-    const int slab = q / NC, c = q - slab * NC;
-    L.x = *(const u32x4*)(xsrc + (long long)c * kFrChunk);
-    const u32x4* ws = (const u32x4*)a.Wq + (long long)q * kFrUnitsW + tid;
+  auto issue_w = [&](int q) {
+    const int slab = q / NC;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(smem0 + (uint32_t)((q % kFrWBufs) * kFrWBuf));
+    const u32x4* ws = (const u32x4*)a.Wq + (long long)q * kFrUnitsW + w * kWave + lane;
 #pragma unroll
-    for (int i = 0; i < kFrUnitsW / kFrThreads; ++i) L.w[i] = ws[i * kFrThreads];
-    L.b = a.biasq[(long long)slab * kFrSlab + tid];
-  };
-  auto stage = [&](const Ld& L, int buf) {
-    char* base = smem + buf * kFrBuf;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    *(u32x4*)(base + xdst) = xok ? L.x : zero;
-    u32x4* wd = (u32x4*)(base + kFrXBytes) + tid;
-#pragma unroll
-    for (int i = 0; i < kFrUnitsW / kFrThreads; ++i) wd[i * kFrThreads] = L.w[i];
-    ((float*)(base + kFrXBytes + kFrWBytes))[tid] = L.b;
+    for (int i = 0; i < kFrUnitsW / kFrThreads; ++i)
+      fr_dma16(ws + i * kFrThreads, base + (i * kFrThreads + w * kWave) * 16);
+    fr_dma4(a.biasq + (long long)slab * kFrSlab + (w & 3) * kWave + lane,
+            base + kFrWBytes + (w >> 2) * kFrBBytes + (w & 3) * kWave * 4);
   };
 
   floatx16 acc[2][4];
   auto reset = [&](int buf) {
-    const float* bs = (const float*)(smem + buf * kFrBuf + kFrXBytes + kFrWBytes);
+    const float* bs = (const float*)(smem + buf * kFrWBuf + kFrWBytes);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const floatx16 bv = *(const floatx16*)(bs + ((4 * we + t) * 2 + hf) * 16);
@@ -159,9 +196,9 @@ __global__ __launch_bounds__(kFrThreads) void fr_tiled_kernel(FrTiledArgs a) {
       acc[1][t] = bv;
     }
   };
-  auto compute = [&](int buf) {
-    const bf16x8* xs = (const bf16x8*)(smem + buf * kFrBuf);
-    const bf16x8* ws = (const bf16x8*)(smem + buf * kFrBuf + kFrXBytes);
+  auto compute = [&](int wbuf, int xbuf) {
+    const bf16x8* xs = (const bf16x8*)(smem + kFrWBufs * kFrWBuf + xbuf * kFrXBytes);
+    const bf16x8* ws = (const bf16x8*)(smem + wbuf * kFrWBuf);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const bf16x8 b0 = xs[((2 * wt + 0) * 2 + s) * kWave + lane];
@@ -201,31 +238,35 @@ __global__ __launch_bounds__(kFrThreads) void fr_tiled_kernel(FrTiledArgs a) {
     fr_fold<K, FULL>(T[1], P[1], mr[1], zr[1], acc[1][2], pb + 2 * kTile, hi);
     fr_fold<K, FULL>(T[1], P[1], mr[1], zr[1], acc[1][3], pb + 3 * kTile, hi);
   };
-  // two LDS buffers; the loads of a chunk are issued two chunks before it is
-  // staged.  A slab has an even number of chunks, so it starts in buffer 0,
-  // which then also holds its bias.
-  Ld L0, L1;
-  fetch(0, L0);
-  fetch(1, L1);
-  stage(L0, 0);
-  __syncthreads();
+  // One barrier per chunk.  Loads are issued in the order X(0), W(0), X(1..4),
+  // W(1), then per chunk q: X(q + 5), W(q + 2); so X(q) always precedes W(q),
+  // and before chunk q at most the loads of the previous iteration (X(q + 4):
+  // 2, W(q + 1): 3) may still fly.  The wait + barrier make chunk q visible
+  // and free the buffers of chunk q - 1.
+  issue_x(0);
+  issue_w(0);
+  for (int q = 1; q < 5 && q < Q; ++q) issue_x(q);
+  if (Q > 1) issue_w(1);
   for (int slab = 0; slab < a.nslab; ++slab) {
-    reset(0);
-    for (int c = 0; c < NC; c += 2) {
+    for (int c = 0; c < NC; ++c) {
       const int q = slab * NC + c;
-      if (q + 2 < Q) fetch(q + 2, L0);
-      compute(0);
-      stage(L1, 1);
-      __syncthreads();
-      if (q + 3 < Q) fetch(q + 3, L1);
-      compute(1);
-      if (q + 2 < Q) stage(L0, 0);
-      __syncthreads();
+      if (q + 4 < Q)
+        fr_publish<kVmcnt5>();
+      else if (q + 1 < Q)
+        fr_publish<kVmcnt3>();
+      else
+        fr_publish<kVmcnt0>();
+      if (q + 5 < Q) issue_x(q + 5);
+      if (q + 2 < Q) issue_w(q + 2);
+      const int wbuf = q % kFrWBufs;
+      if (c == 0) reset(wbuf);
+      compute(wbuf, q % kFrXBufs);
     }
     fold(slab);
   }
+  __syncthreads();
 
-  // merge the 8 lists of every token (layout [list][slot][token] and
+  // merge the 4 lists of every token (layout [list][slot][token] and
   // [list][token]: consecutive tokens on consecutive addresses)
   float2* ml = (float2*)smem;
   float2* mz = ml + kFrLists * K * kFrTokens;

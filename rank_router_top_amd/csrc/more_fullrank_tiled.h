@@ -6,21 +6,22 @@
 // (softmax over the k selected) or eq. (6) with the normaliser of eq. (8).
 //
 // The full-rank product is a dense contraction (2 N h M flops, K = h), so it
-// is tiled like a GEMM.  One workgroup (8 waves) owns 128 tokens and sweeps
-// the experts in slabs of 512; over K it streams 32-wide chunks of its X block
-// (8 KiB) and of the slab's weights (32 KiB) through two LDS buffers, loads
-// issued two chunks ahead.  Wave (wt, we) accumulates tokens 64 wt .. +64
-// (two 32-token groups) against experts 128 we .. +128 of the slab (four
-// 32-expert tiles): eight 32x32 fp32 accumulators, 16 v_mfma_f32_32x32x16_bf16
-// per chunk against 12 LDS operand reads.  At the end of a slab every lane
-// (token column, half hf) folds its 16 logits per tile into a register top-k
-// list (value desc, expert asc) and, for eq. (6), the running maximum and
-// normaliser of eq. (8); at the end of the sweep the 8 lists of each token
-// (4 expert quarters x 2 halves) are merged through LDS.
+// is tiled like a GEMM.  One workgroup (8 waves) owns 256 tokens and sweeps
+// the experts in slabs of 256; over K it streams 32-wide chunks of its X block
+// (16 KiB) and of the slab's weights (16 KiB) straight from global memory into
+// LDS rings.  Wave (wt, we) accumulates tokens 64 wt .. +64 (two 32-token
+// groups) against experts 128 we .. +128 of the slab (four 32-expert tiles):
+// eight 32x32 fp32 accumulators, 16 v_mfma_f32_32x32x16_bf16 per chunk
+// against 12 LDS operand reads.  The square tile keeps the operand bytes per
+// flop at their minimum for the accumulators a CU holds.  At the end of a
+// slab every lane (token column, half hf) folds its 16 logits per tile into a
+// register top-k list (value desc, expert asc) and, for eq. (6), the running
+// maximum and normaliser of eq. (8); at the end of the sweep the 4 lists of
+// each token (2 expert halves x 2 lane halves) are merged through LDS.
 //
 // Weights are packed per call by fr_pack_kernel in natural expert order:
 // unit (slab, chunk, tile, kstep, lane) holds the 8 bf16 W[k][j] of the
-// 32x32x16 A operand, j = 512 slab + 32 tile + lane % 32,
+// 32x32x16 A operand, j = 256 slab + 32 tile + lane % 32,
 // k = 32 chunk + 16 kstep + 8 (lane / 32) + e; rows past M and columns past h
 // are zero, and the bias in accumulator layout is -inf past M.
 #pragma once
@@ -30,15 +31,15 @@
 namespace more {
 
 constexpr int kFrWaves = 8;          // waves per workgroup
-constexpr int kFrTokens = 128;       // tokens per workgroup
-constexpr int kFrSlab = 512;         // experts per slab
+constexpr int kFrTokens = 256;       // tokens per workgroup
+constexpr int kFrSlab = 256;         // experts per slab
 constexpr int kFrChunk = 32;         // K per LDS chunk (two MFMA K-steps)
 constexpr int kFrKmax = 8;           // largest k of the tiled kernel
 
 struct FrTiledArgs {
   const uint16_t* X;      // N x h bf16
   const uint16_t* Wq;     // packed weights (see above)
-  const float* biasq;     // [nslab][16][2][16]
+  const float* biasq;     // [nslab][8][2][16]
   int* out_idx;
   float* out_gate;
   float* out_logit;
