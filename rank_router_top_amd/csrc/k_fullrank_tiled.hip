@@ -196,18 +196,40 @@ __global__ __launch_bounds__(kFrThreads) void fr_tiled_kernel(FrTiledArgs a) {
       acc[1][t] = bv;
     }
   };
-  auto compute = [&](int wbuf, int xbuf) {
+  // One chunk: the 12 operand reads, then the 16 MFMAs with the loads of later
+  // chunks (X(qx): 2, W(qw): 3, in that order) spread between them, so that a
+  // wave never issues a burst of loads while its MFMAs wait.
+  auto compute = [&](int wbuf, int xbuf, int qx, int qw) {
     const bf16x8* xs = (const bf16x8*)(smem + kFrWBufs * kFrWBuf + xbuf * kFrXBytes);
     const bf16x8* ws = (const bf16x8*)(smem + wbuf * kFrWBuf);
+    bf16x8 bo[2][2], ao[2][4];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8 b0 = xs[((2 * wt + 0) * 2 + s) * kWave + lane];
-      const bf16x8 b1 = xs[((2 * wt + 1) * 2 + s) * kWave + lane];
+      bo[s][0] = xs[((2 * wt + 0) * 2 + s) * kWave + lane];
+      bo[s][1] = xs[((2 * wt + 1) * 2 + s) * kWave + lane];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 av = ws[((4 * we + t) * 2 + s) * kWave + lane];
-        acc[0][t] = mfma_bf16(av, b0, acc[0][t]);
-        acc[1][t] = mfma_bf16(av, b1, acc[1][t]);
+      for (int t = 0; t < 4; ++t) ao[s][t] = ws[((4 * we + t) * 2 + s) * kWave + lane];
+    }
+    const bool dox = qx < Q, dow = qw < Q;
+    const uint32_t xl = __builtin_amdgcn_readfirstlane(smem0 + (uint32_t)(kFrWBufs * kFrWBuf + (qx % kFrXBufs) * kFrXBytes)) +
+                        2 * w * kWave * 16;
+    const uint16_t* xg = xsrc + (long long)(qx % NC) * kFrChunk;
+    const uint32_t wb = __builtin_amdgcn_readfirstlane(smem0 + (uint32_t)((qw % kFrWBufs) * kFrWBuf));
+    const u32x4* wg = (const u32x4*)a.Wq + (long long)qw * kFrUnitsW + w * kWave + lane;
+    const float* bg = a.biasq + (long long)(qw / NC) * kFrSlab + (w & 3) * kWave + lane;
+    static_assert(kFrUnitsW / kFrThreads == 2, "two weight loads per lane and chunk");
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int s = m >> 3, t = (m >> 1) & 3, g = m & 1;
+      acc[g][t] = mfma_bf16(ao[s][t], bo[s][g], acc[g][t]);
+      if (m == 1 || m == 4 || m == 7 || m == 10 || m == 13) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (m == 1 && dox) fr_dma16(xg, xl);
+        if (m == 4 && dox) fr_dma16(xg + 16, xl + kWave * 16);
+        if (m == 7 && dow) fr_dma16(wg, wb + w * kWave * 16);
+        if (m == 10 && dow) fr_dma16(wg + kFrThreads, wb + (kFrThreads + w * kWave) * 16);
+        if (m == 13 && dow) fr_dma4(bg, wb + kFrWBytes + (w >> 2) * kFrBBytes + (w & 3) * kWave * 4);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -256,11 +278,9 @@ __global__ __launch_bounds__(kFrThreads) void fr_tiled_kernel(FrTiledArgs a) {
         fr_publish<kVmcnt3>();
       else
         fr_publish<kVmcnt0>();
-      if (q + 5 < Q) issue_x(q + 5);
-      if (q + 2 < Q) issue_w(q + 2);
       const int wbuf = q % kFrWBufs;
       if (c == 0) reset(wbuf);
-      compute(wbuf, q % kFrXBufs);
+      compute(wbuf, q % kFrXBufs, q + 5, q + 2);
     }
     fold(slab);
   }
