@@ -84,6 +84,21 @@ def test_empty_batch_is_a_noop():
     assert call_lowrank(N=0, X=None, idx=None, g=None) == 0
 
 
+def test_fullrank_workspace_covers_the_tiled_layout():
+    """bf16 with k <= 8 and h a multiple of 64 runs the LDS-tiled kernel: W
+    packed per 256-expert slab (h x 256 bf16 each) plus the bias in
+    accumulator layout (256 fp32 per slab), past the plain layout's size."""
+    bf = R.MORE_DT_BF16
+    for h, M in ((2048, 4096), (128, 1000), (64, 192), (256, 513)):
+        nslab = (M + 255) // 256
+        need = nslab * 256 * h * 2 + nslab * 256 * 4
+        for k in (1, 8):
+            assert R.workspace_bytes(True, bf, 100, h, 0, M, k, 0, True) >= need
+    # shapes of the plain kernel keep its own size
+    assert R.workspace_bytes(True, bf, 100, 96, 0, 300, 8, 0, True) > 0
+    assert R.workspace_bytes(True, bf, 100, 128, 0, 700, 16, 0, True) > 0
+
+
 def test_fullrank_rejects_bad_arguments():
     L = R.lib()
     f = L.more_route_fullrank
