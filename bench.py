@@ -94,11 +94,13 @@ def parse():
 def source_hash():
     """Hash of the HIP sources the routing call is built from: traffic counters
     taken on another version of its kernels are not reported.  The files that
-    hold only the balancing, dispatch and backward kernels are left out."""
+    hold only the balancing, dispatch, backward and full-rank kernels are left
+    out."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_router_top_amd", "csrc")
-    other = {"k_backward.hip", "more_backward.h", "k_balance.hip", "more_balance.h", "k_sort.hip", "more_sort.h"}
+    other = {"k_backward.hip", "more_backward.h", "k_balance.hip", "more_balance.h", "k_sort.hip", "more_sort.h",
+             "k_fullrank.hip", "more_fullrank.h", "k_fullrank_tiled.hip", "more_fullrank_tiled.h"}
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".h", ".hip")) and name not in other:
             with open(os.path.join(csrc, name), "rb") as f:

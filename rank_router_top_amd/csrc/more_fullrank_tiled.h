@@ -54,9 +54,11 @@ inline size_t fr_tiled_bytes(long long h, long long M) {
   return (size_t)(nslab * kFrSlab * h * 2) + (size_t)(nslab * kFrSlab * 4);
 }
 
-// Whether the tiled kernel covers the call (bf16 only).
+// Whether the tiled kernel covers the call (bf16 only; the chunk count
+// (M / kFrSlab) (h / kFrChunk) stays well inside int).
 inline bool fr_tiled_supported(long long h, long long M, int k) {
-  return h % (2 * kFrChunk) == 0 && k <= kFrKmax && M >= 1;
+  return h % (2 * kFrChunk) == 0 && k <= kFrKmax && M >= 1 &&
+         ((M + kFrSlab - 1) / kFrSlab) * (h / kFrChunk) < (1LL << 30);
 }
 
 // Packs W (h x M bf16) and the bias into `ws` (fr_tiled_bytes(h, M) bytes,
