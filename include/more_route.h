@@ -243,7 +243,11 @@ size_t more_backward_workspace_bytes(more_dtype dt, int64_t N, int64_t h, int64_
  * gates with l = x W + b (§2 standard router; App. H.3 Fig. 20 fuses it the
  * same way, reloading weight tiles instead of a rank-r intermediate).
  *   W  h x M.  Other arguments as for more_route_lowrank.
- *   workspace  size from more_route_workspace_bytes(1, ...).
+ *   workspace  size from more_route_workspace_bytes(1, ...): W and the bias
+ *              are repacked into it on every call (overwritten).
+ * bf16 with k <= 8 and h % 64 == 0 runs an LDS-tiled MFMA sweep (256 tokens
+ * per workgroup, 256-expert slabs); other shapes and fp32 run a plain
+ * one-wave-per-32-tokens kernel.  Both give the same selection rule.
  */
 more_status more_route_fullrank(more_dtype dt, const void* X, int64_t N, int64_t h, const void* W,
                                 int64_t M, const float* bias, int32_t k, more_gate gate,
