@@ -1,0 +1,26 @@
+"""Host-side checks of the benchmark script: the one-GPU contract and the
+committed HBM traffic record it reports from."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+def test_traffic_record_is_consistent():
+    with open(os.path.join(ROOT, "profiles", "traffic_headline.json")) as f:
+        tr = json.load(f)
+    assert abs(tr["bytes_per_launch"] - tr["fetch_bytes"] - tr["write_bytes"]) < 1.0
+    # X is read once and the outputs written once at least
+    assert tr["bytes_per_launch"] >= tr["algorithmic_bytes"]
+    assert abs(tr["traffic_over_algorithmic"] - tr["bytes_per_launch"] / tr["algorithmic_bytes"]) < 1e-9
+    assert len(tr["source_hash"]) == 16
