@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--no-balance", action="store_true")
     ap.add_argument("--no-dispatch", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-sharded", action="store_true")
+    ap.add_argument("--shards", type=int, default=8)
     ap.add_argument("--fullrank-steps", type=int, default=3)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, "
@@ -94,13 +96,14 @@ def parse():
 def source_hash():
     """Hash of the HIP sources the routing call is built from: traffic counters
     taken on another version of its kernels are not reported.  The files that
-    hold only the balancing, dispatch, backward and full-rank kernels are left
-    out."""
+    hold only the balancing, dispatch, backward, full-rank and shard-merge
+    kernels are left out."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_router_top_amd", "csrc")
     other = {"k_backward.hip", "more_backward.h", "k_balance.hip", "more_balance.h", "k_sort.hip", "more_sort.h",
-             "k_fullrank.hip", "more_fullrank.h", "k_fullrank_tiled.hip", "more_fullrank_tiled.h"}
+             "k_fullrank.hip", "more_fullrank.h", "k_fullrank_tiled.hip", "more_fullrank_tiled.h",
+             "k_merge.hip", "more_merge.h"}
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".h", ".hip")) and name not in other:
             with open(os.path.join(csrc, name), "rb") as f:
@@ -390,6 +393,51 @@ def main():
             "roofline": {"bound": "hbm", "achieved": d_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": d_ach / HBM_PEAK_GBS, "algorithmic_bytes_per_call": d_bytes}}
         del dws, dout
+
+    if not args.no_sharded and cfg.M % args.shards == 0 and cfg.M // args.shards >= cfg.k:
+        # Experts sharded over G GPUs: each GPU routes all N tokens over its
+        # M / G experts (timed here at that real shape), then, after an
+        # all-to-all of the candidates, merges N / G tokens' G lists; the
+        # merge is timed here over all N tokens' lists.
+        G = args.shards
+        width = cfg.M // G
+        nbs = R.workspace_bytes(False, dt, cfg.N, cfg.h, cfg.r, width, cfg.k, gate, True)
+        wss = torch.empty(nbs, dtype=torch.uint8, device=dev)
+        cand_l = torch.empty((G, cfg.N, cfg.k), dtype=torch.float32, device=dev)
+        cand_i = torch.empty((G, cfg.N, cfg.k), dtype=torch.int32, device=dev)
+        for g in range(G):
+            R.pack_lowrank(R1, R2[:, g * width:(g + 1) * width].contiguous(),
+                           b[g * width:(g + 1) * width].contiguous(), wss, stream=stream)
+            so = R.route_lowrank_packed(X, cfg.r, width, cfg.k, gate, wss, stream=stream)
+            cand_l[g].copy_(so["logit"])
+            cand_i[g].copy_(so["idx"])
+        torch.cuda.synchronize()
+
+        def shard_call():   # shard G - 1 is packed in wss
+            R.route_lowrank_packed(X, cfg.r, width, cfg.k, gate, wss, out=so, stream=stream)
+
+        def merge_call():
+            return R.topk_merge(cand_l, cand_i, None, cfg.M, width, gate, want_logit=False, stream=stream)
+
+        for _ in range(3):
+            shard_call()
+            mo = merge_call()
+        s_mean = time_events(torch, shard_call, max(args.steps, 20), stream)[0]
+        m_mean, m_med, m_p10, m_p90 = time_events(torch, merge_call, max(args.steps, 20), stream)
+        kernel_only()
+        torch.cuda.synchronize()
+        mism = int((mo["idx"] != out["idx"]).any(dim=1).sum())
+        m_bytes = cfg.N * (G * cfg.k * 8 + cfg.k * 8)
+        m_ach = m_bytes / (m_mean * 1e-3) / 1e9
+        log(f"sharded: {G} shards of {width} experts, shard call {s_mean:.4f} ms, merge {m_mean:.4f} ms, "
+            f"{mism} tokens differ from the unsharded call")
+        result["sharded"] = {
+            "entry": "more_topk_merge", "shards": G, "shard_width": width,
+            "shard_call_ms": s_mean, "merge_ms": m_mean, "merge_ms_p10": m_p10, "merge_ms_p90": m_p90,
+            "tokens_differing_from_unsharded": mism,
+            "merge_roofline": {"bound": "hbm", "achieved": m_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": m_ach / HBM_PEAK_GBS, "algorithmic_bytes_per_call": m_bytes}}
+        del wss, cand_l, cand_i
 
     if not args.no_fullrank:
         FR = CF.FULLRANK

@@ -239,6 +239,33 @@ more_status more_lowrank_backward_packed(more_dtype dt, const void* X, int64_t N
 size_t more_backward_workspace_bytes(more_dtype dt, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k);
 
 /*
+ * Top-k over expert shards: merges per-shard candidate lists into the
+ * token's top k and gates (App. E.3: a hierarchical top-k over shards of the
+ * experts; gates as Fig. 12 or eq. (6) with the normaliser of eq. (8)).
+ * The M experts are cut into G = ceil(M / shard_width) shards of
+ * shard_width consecutive experts (the last may be shorter); shard g covers
+ * experts g * shard_width ..  Each shard routes every token over its own
+ * experts (more_route_lowrank / more_lowrank_route_packed with that shard's
+ * columns of R2 and entries of the bias, or more_route_fullrank) and hands
+ * over its topk_logit and topk_idx (shard-local indices) and, for
+ * MORE_GATE_FULL_SOFTMAX, its lse.
+ *   cand_logit  G x N x k fp32: shard g's logits, each row ordered by
+ *               (logit desc, index asc) as the routing calls write them.
+ *   cand_idx    G x N x k int32: shard-local expert indices.
+ *   shard_lse   G x N fp32 (MORE_GATE_FULL_SOFTMAX) or NULL (TOPK).
+ *   topk_idx, topk_gate (N x k, required), topk_logit (N x k, NULL to skip),
+ *   lse (N, full-softmax gates only, NULL to skip): as for more_route_lowrank;
+ *   global expert indices, ordered by (logit desc, index asc).
+ * Requires 1 <= k <= MORE_MAX_K, k <= shard_width and at least k experts in
+ * the last shard (else MORE_ERR_BAD_K).  The caller owns every buffer; the
+ * call allocates nothing and enqueues one kernel on `stream`.  N = 0 is a
+ * no-op.
+ */
+more_status more_topk_merge(int64_t N, int64_t M, int64_t shard_width, int32_t k, more_gate gate,
+                            const float* cand_logit, const int32_t* cand_idx, const float* shard_lse,
+                            int32_t* topk_idx, float* topk_gate, float* topk_logit, float* lse, void* stream);
+
+/*
  * Fused standard (full-rank) router + top-k + gates: the same selection and
  * gates with l = x W + b (§2 standard router; App. H.3 Fig. 20 fuses it the
  * same way, reloading weight tiles instead of a rank-r intermediate).

@@ -20,6 +20,7 @@
 #include "more_pack.h"
 #include "more_dispatch.h"
 #include "more_fullrank_tiled.h"
+#include "more_merge.h"
 #include "more_balance.h"
 #include "more_sort.h"
 #include "more_backward.h"
@@ -742,6 +743,32 @@ more_status more_dispatch_sort(const int32_t* topk_idx, int64_t N, int32_t k, in
   }
   return launch_dispatch_sort(topk_idx, n, (int)M, sorted_expert, sorted_slot, offsets, hist, tk, tv,
                               (hipStream_t)stream) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+}
+
+more_status more_topk_merge(int64_t N, int64_t M, int64_t shard_width, int32_t k, more_gate gate,
+                            const float* cand_logit, const int32_t* cand_idx, const float* shard_lse,
+                            int32_t* topk_idx, float* topk_gate, float* topk_logit, float* lse, void* stream) {
+  if (gate != MORE_GATE_TOPK_SOFTMAX && gate != MORE_GATE_FULL_SOFTMAX) return MORE_ERR_BAD_GATE;
+  if (N < 0 || N > (1LL << 40) || M < 1 || M > (1 << 24) || shard_width < 1) return MORE_ERR_BAD_SHAPE;
+  if (k < 1 || k > MORE_MAX_K || (int64_t)k > shard_width) return MORE_ERR_BAD_K;
+  const int64_t G = (M + shard_width - 1) / shard_width;
+  if (M - (G - 1) * shard_width < k) return MORE_ERR_BAD_K;   // the last shard holds fewer than k experts
+  if (N == 0) return MORE_OK;
+  const bool full = gate == MORE_GATE_FULL_SOFTMAX;
+  if (!cand_logit || !cand_idx || !topk_idx || !topk_gate || (full && !shard_lse)) return MORE_ERR_NULL_ARG;
+  MergeArgs a;
+  a.cand_logit = cand_logit;
+  a.cand_idx = cand_idx;
+  a.shard_lse = shard_lse;
+  a.out_idx = topk_idx;
+  a.out_gate = topk_gate;
+  a.out_logit = topk_logit;
+  a.out_lse = full ? lse : nullptr;
+  a.N = N;
+  a.W = shard_width;
+  a.G = (int)G;
+  a.k = k;
+  return launch_topk_merge(a, full, (hipStream_t)stream) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 
 more_status more_route_fullrank(more_dtype dt, const void* X, int64_t N, int64_t h, const void* W,

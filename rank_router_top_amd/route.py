@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "MORE_OK", 1: "MORE_ERR_NULL_ARG", 2: "MORE_ERR_BAD_SHAPE", 3
 EXPORTS = ("more_route_lowrank", "more_route_fullrank", "more_route_workspace_bytes",
            "more_status_str", "more_abi_version", "more_lowrank_pack", "more_lowrank_route_packed",
            "more_lowrank_balance_packed", "more_balance_workspace_bytes", "more_dispatch_sort",
-           "more_dispatch_workspace_bytes", "more_lowrank_backward_packed", "more_backward_workspace_bytes")
+           "more_dispatch_workspace_bytes", "more_lowrank_backward_packed", "more_backward_workspace_bytes",
+           "more_topk_merge")
 
 _lock = threading.Lock()
 _lib = None
@@ -74,6 +75,8 @@ def lib() -> C.CDLL:
             L.more_balance_workspace_bytes.restype = C.c_size_t
             L.more_route_workspace_bytes.argtypes = [C.c_int, i32, i64, i64, i64, i64, i32, i32, C.c_int]
             L.more_route_workspace_bytes.restype = C.c_size_t
+            L.more_topk_merge.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, p, p, p, p]
+            L.more_topk_merge.restype = C.c_int
             L.more_status_str.argtypes = [C.c_int]
             L.more_status_str.restype = C.c_char_p
             L.more_abi_version.restype = C.c_int
@@ -198,6 +201,26 @@ def balance_lowrank_packed(X, r: int, M: int, k: int, gate: int, workspace, *, o
 
 def dispatch_workspace_bytes(N: int, k: int, M: int) -> int:
     return int(lib().more_dispatch_workspace_bytes(N, k, M))
+
+
+def topk_merge(cand_logit, cand_idx, shard_lse, M: int, shard_width: int, gate: int = MORE_GATE_TOPK_SOFTMAX, *,
+               want_logit: bool = True, want_lse: bool = True, stream=None) -> dict:
+    """more_topk_merge: cand_logit / cand_idx are (G, N, k) device tensors
+    (fp32 / int32, shard-local indices), shard_lse (G, N) fp32 or None.
+    Returns dict(idx, gate, logit, lse) with global expert indices."""
+    import torch
+    G, N, k = cand_logit.shape
+    dev = cand_logit.device
+    full = gate == MORE_GATE_FULL_SOFTMAX
+    o = {"idx": torch.empty((N, k), dtype=torch.int32, device=dev),
+         "gate": torch.empty((N, k), dtype=torch.float32, device=dev),
+         "logit": torch.empty((N, k), dtype=torch.float32, device=dev) if want_logit else None,
+         "lse": torch.empty(N, dtype=torch.float32, device=dev) if (want_lse and full) else None}
+    _check("more_topk_merge", lib().more_topk_merge(
+        N, M, shard_width, k, gate, _ptr(cand_logit.contiguous()), _ptr(cand_idx.contiguous()),
+        _ptr(None if shard_lse is None else shard_lse.contiguous()),
+        _ptr(o["idx"]), _ptr(o["gate"]), _ptr(o["logit"]), _ptr(o["lse"]), _stream(stream)))
+    return o
 
 
 def dispatch_sort(idx, M: int, *, out=None, workspace=None, stream=None) -> dict:

@@ -99,6 +99,23 @@ def test_fullrank_workspace_covers_the_tiled_layout():
     assert R.workspace_bytes(True, bf, 100, 128, 0, 700, 16, 0, True) > 0
 
 
+def test_topk_merge_validation():
+    """The shard merge checks its arguments on the host: gate, shapes, k
+    against the shard width and the last shard, and required pointers; N = 0
+    is a no-op (no HIP call)."""
+    f = R.lib().more_topk_merge
+    FK = FAKE
+    assert f(10, 4096, 512, 8, 7, FK, FK, None, FK, FK, None, None, None) == 5          # gate
+    assert f(-1, 4096, 512, 8, 0, FK, FK, None, FK, FK, None, None, None) == 2          # N
+    assert f(10, 4096, 0, 8, 0, FK, FK, None, FK, FK, None, None, None) == 2            # width
+    assert f(10, 4096, 4, 8, 0, FK, FK, None, FK, FK, None, None, None) == 3            # k > width
+    assert f(10, 1000, 300, 200, 0, FK, FK, None, FK, FK, None, None, None) == 3        # last shard 100 < k
+    assert f(10, 4096, 512, 33, 0, FK, FK, None, FK, FK, None, None, None) == 3         # k > MORE_MAX_K
+    assert f(10, 4096, 512, 8, 0, None, FK, None, FK, FK, None, None, None) == 1        # candidates
+    assert f(10, 4096, 512, 8, 1, FK, FK, None, FK, FK, None, None, None) == 1          # full gate needs lse
+    assert f(0, 4096, 512, 8, 0, None, None, None, None, None, None, None, None) == 0   # N = 0
+
+
 def test_fullrank_rejects_bad_arguments():
     L = R.lib()
     f = L.more_route_fullrank
