@@ -67,9 +67,95 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (FULL && a.out_lse) a.out_lse[n] = lse;
 }
 
+// k == KMAX (4, 8 or 16) with 16-byte aligned candidate arrays: a lane
+// reads its token's lists with 16-byte loads, the next shard's while it
+// merges the current one.
+template <int KMAX, bool FULL>
+__global__ __launch_bounds__(256) void merge_vec_kernel(MergeArgs a) {
+  constexpr int C = KMAX / 4;
+  const long long n = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (n >= a.N) return;
+  float V[KMAX];
+  int IX[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    V[j] = -__builtin_inff();
+    IX[j] = 0x7fffffff;
+  }
+  float4 lc[C], ln[C];
+  int4 ic[C], in_[C];
+  auto load = [&](int g, float4 (&l)[C], int4 (&ix)[C]) {
+    const size_t base = ((size_t)g * a.N + n) * KMAX;
+    const float4* lp = (const float4*)(a.cand_logit + base);
+    const int4* ip = (const int4*)(a.cand_idx + base);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      l[c] = lp[c];
+      ix[c] = ip[c];
+    }
+  };
+  load(0, lc, ic);
+  for (int g = 0; g < a.G; ++g) {
+    if (g + 1 < a.G) load(g + 1, ln, in_);
+    const int off = (int)((long long)g * a.W);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const float x[4] = {lc[c].x, lc[c].y, lc[c].z, lc[c].w};
+      const int ix[4] = {ic[c].x, ic[c].y, ic[c].z, ic[c].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (x[e] >= V[KMAX - 1]) ordered_insert<KMAX>(V, IX, x[e], off + ix[e]);
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      lc[c] = ln[c];
+      ic[c] = in_[c];
+    }
+  }
+  float lse = 0.f;
+  if (FULL) {
+    float mm = -__builtin_inff();
+    for (int g = 0; g < a.G; ++g) mm = fmaxf(mm, a.shard_lse[(size_t)g * a.N + n]);
+    float z = 0.f;
+    for (int g = 0; g < a.G; ++g) z += __builtin_amdgcn_exp2f((a.shard_lse[(size_t)g * a.N + n] - mm) * kLog2e);
+    lse = mm + __builtin_amdgcn_logf(z) * kLn2;
+  }
+  float w[KMAX];
+  float denom = 0.f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    w[j] = __builtin_amdgcn_exp2f((V[j] - (FULL ? lse : V[0])) * kLog2e);
+    denom += w[j];
+  }
+  const float inv = FULL ? 1.f : 1.f / denom;
+  float4* og = (float4*)(a.out_gate + (size_t)n * KMAX);
+  int4* oi = (int4*)(a.out_idx + (size_t)n * KMAX);
+  float4* ol = a.out_logit ? (float4*)(a.out_logit + (size_t)n * KMAX) : nullptr;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    oi[c] = make_int4(IX[4 * c], IX[4 * c + 1], IX[4 * c + 2], IX[4 * c + 3]);
+    og[c] = make_float4(w[4 * c] * inv, w[4 * c + 1] * inv, w[4 * c + 2] * inv, w[4 * c + 3] * inv);
+    if (ol) ol[c] = make_float4(V[4 * c], V[4 * c + 1], V[4 * c + 2], V[4 * c + 3]);
+  }
+  if (FULL && a.out_lse) a.out_lse[n] = lse;
+}
+
+static bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; }
+
 template <int KMAX>
 static hipError_t launch_k(const MergeArgs& a, bool full, hipStream_t s) {
   const dim3 grid((unsigned)((a.N + 255) / 256));
+  if constexpr (KMAX <= 16) {   // larger lists spill in the 16-byte form
+    const bool vec = a.k == KMAX && aligned16(a.cand_logit) && aligned16(a.cand_idx) && aligned16(a.out_idx) &&
+                     aligned16(a.out_gate) && aligned16(a.out_logit);
+    if (vec) {
+      if (full)
+        hipLaunchKernelGGL((merge_vec_kernel<KMAX, true>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((merge_vec_kernel<KMAX, false>), grid, dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (full)
     hipLaunchKernelGGL((merge_kernel<KMAX, true>), grid, dim3(256), 0, s, a);
   else

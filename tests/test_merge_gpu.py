@@ -80,7 +80,7 @@ def test_sharded_ties_lower_index_wins(oracle_lib):
     R2f[:, dup] = R2f[:, src]
     bf[dup] = bf[src]
     R2 = I.f32_to_bf16_bits(R2f)
-    for k in (1, 8):
+    for k in (1, 5, 8, 16):   # 5: the scalar form with filler slots; 8, 16: the 16-byte form
         for gate in (CF.GATE_TOPK_SOFTMAX, CF.GATE_FULL_SOFTMAX):
             say(f"ties k={k} gate={gate}")
             g = sharded_route(X, R1, R2, bf, k, gate, width)
