@@ -29,6 +29,12 @@ resident in HBM.  Prints ONE JSON line:
                  the routing call returned -> expert-sorted slots + offsets),
                  HIP-event timed, algorithmic bytes (read N k indices, write
                  N k experts + N k slots + M + 1 offsets) against 8 TB/s
+  sharded        experts cut into --shards shards (default 8): one shard's
+                 routing call at the full N (one GPU's share of the routing)
+                 and more_topk_merge over all N tokens' shard lists, HIP-event
+                 timed, the merge against 8 TB/s over its algorithmic bytes,
+                 plus the count of tokens whose merged selection differs
+                 from the unsharded call
   context        published B200 figures of the paper (other hardware)
 Only one GPU is supported: --gpus above 1 exits with a message.
 """
