@@ -15,7 +15,11 @@ resident in HBM.  Prints ONE JSON line:
   pct_roofline   roofline time / step time, roofline time = max(X bytes / 8 TB/s,
                  2N(hr + rM) / 2.5 PFLOP/s)
   cpu_baseline   the fp64 oracle on a bounded sample of the same tokens, timed
-                 on the host cores (rank 0, one GPU only)
+                 on the host cores (one thread on the first 4096 tokens, then
+                 every thread; the CPU model is named)
+  parity         the parity rule applied to the GPU routing call's results over
+                 the oracle's sample (all N tokens when it fits the CPU budget):
+                 gap-clear mismatches (0 expected) and the full rule
   fullrank       the fused full-rank (standard) router on the same tokens
   balance        the training forward with balancing statistics
                  (more_lowrank_balance_packed: routing with the full-softmax
@@ -207,6 +211,56 @@ def time_events(torch, fn, steps, stream):
     return sum(ms) / len(ms), ms[len(ms) // 2], ms[len(ms) // 10], ms[(9 * len(ms)) // 10]
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_leg(args, cfg, gate, X_np, R1_np, R2_np, b_np, ref):
+    """The fp64 oracle on the host cores: one thread on the first 4096 tokens
+    (per-core rate), then every thread on a sample of about --cpu-seconds of
+    work (all N tokens when that fits), and the parity rule applied to the
+    GPU routing call's results over that sample."""
+    import numpy as np
+
+    import oracle
+    from oracle import parity as P
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    n1 = min(4096, cfg.N)
+    t = time.perf_counter()
+    oracle.route_lowrank(X_np[:n1], R1_np, R2_np, b_np, cfg.k, gate, nthreads=1)
+    one = n1 / (time.perf_counter() - t)
+    n = int(min(cfg.N, max(n1, args.cpu_seconds * one * threads)))
+    t = time.perf_counter()
+    o = oracle.route_lowrank(X_np[:n], R1_np, R2_np, b_np, cfg.k, gate, nthreads=threads)
+    dt_cpu = time.perf_counter() - t
+    log(f"cpu oracle {n / dt_cpu:.0f} tokens/s on {threads} threads, {one:.0f} tokens/s on one")
+    cpu = {"value": n / dt_cpu, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(), "one_thread_tokens_per_s": one, "one_thread_sample": f"first {n1} tokens",
+           "sample": f"first {n} of the {cfg.N} tokens, same weights, fp64, {dt_cpu:.1f} s wall"}
+    gpu = {key: (None if v is None else v[:n]) for key, v in ref.items()}
+    at = oracle.logits_at(X_np[:n], R1_np, R2_np, b_np, gpu["idx"], nthreads=threads)
+    par = {"tokens": n, "rule": "gap-clear index sets identical, gates within 1e-3; every index tied to its own "
+                                "oracle logit and gate",
+           "gap_clear_mismatches": P.mismatches(o, gpu["idx"])}
+    try:
+        par.update(P.compare(o, gpu, cfg.k, gate == 1, 2e-4, "bench", at))
+        par["pass"] = True
+    except AssertionError as e:
+        par["pass"] = False
+        par["failure"] = str(e)[:300]
+    par["max_gate_error"] = float(np.max(np.abs(gpu["gate"].astype(np.float64) - o["gate"])))
+    log(f"parity over {n} tokens: {par}")
+    return cpu, par
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -273,6 +327,11 @@ def main():
 
     p_mean = time_events(torch, pack_only, 20, stream)[0]
     log(f"routing call mean {k_mean:.4f} ms (p10 {k_p10:.4f}, p90 {k_p90:.4f}); pack {p_mean:.4f} ms")
+
+    # the routing call's results over all N (logits too), for the parity check of the CPU leg
+    ref = R.route_lowrank_packed(X, cfg.r, cfg.M, cfg.k, gate, ws, stream=stream)
+    torch.cuda.synchronize()
+    ref = {key: (None if v is None else v.cpu().numpy()) for key, v in ref.items()}
 
     alg_bytes = algorithmic_bytes(cfg, cfg.k, False)
     achieved = alg_bytes / (k_mean * 1e-3) / 1e9
@@ -467,22 +526,7 @@ def main():
         del W, wsw
 
     if not args.no_cpu:
-        import oracle
-        oracle.build(force=False)
-        threads = oracle.max_threads()
-        n0 = 1024
-        t = time.perf_counter()
-        oracle.route_lowrank(X_np[:n0], R1_np, R2_np, b_np, cfg.k, gate, nthreads=threads)
-        per_tok = (time.perf_counter() - t) / n0
-        n = int(min(cfg.N, max(n0, args.cpu_seconds / max(per_tok, 1e-9))))
-        t = time.perf_counter()
-        oracle.route_lowrank(X_np[:n], R1_np, R2_np, b_np, cfg.k, gate, nthreads=threads)
-        dt_cpu = time.perf_counter() - t
-        result["cpu_baseline"] = {"value": n / dt_cpu, "unit": "tokens/s", "cores": threads,
-                                  "kind": "oracle",
-                                  "sample": f"first {n} of the {cfg.N} tokens, same weights, fp64, "
-                                            f"{dt_cpu:.1f} s wall"}
-        log(f"cpu oracle {n / dt_cpu:.0f} tokens/s on {threads} threads")
+        result["cpu_baseline"], result["parity"] = cpu_leg(args, cfg, gate, X_np, R1_np, R2_np, b_np, ref)
 
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

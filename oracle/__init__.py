@@ -17,9 +17,9 @@ statistics' final formulas and the dispatch sort are plain numpy in
 ``oracle.py``.
 """
 from .oracle import (DT_BF16, DT_F32, DT_F64, GATE_FULL, GATE_TOPK, backward_lowrank, balance_lowrank,
-                     balance_stats, build, dispatch_sort, library_path, logits, max_threads, route_fullrank, route_lowrank,
+                     balance_stats, build, dispatch_sort, library_path, logits, logits_at, max_threads, route_fullrank, route_lowrank,
                      softmax_colsum)
 
 __all__ = ["DT_BF16", "DT_F32", "DT_F64", "GATE_FULL", "GATE_TOPK", "backward_lowrank", "balance_lowrank", "balance_stats",
-           "build", "dispatch_sort", "library_path", "logits", "max_threads", "route_fullrank", "route_lowrank",
+           "build", "dispatch_sort", "library_path", "logits", "logits_at", "max_threads", "route_fullrank", "route_lowrank",
            "softmax_colsum"]

@@ -227,6 +227,62 @@ int oracle_logits(int dt, const void* X, int64_t N, int64_t h, const void* A, in
 }
 
 /*
+ * Logits of chosen experts: out[n * k + j] = l_{n, idx[n k + j]}, the same
+ * definition as oracle_logits (z = x R1, l = z R2 + b, or l = x W + b for
+ * full rank) evaluated only at the k given experts of each token, so that a
+ * selection made elsewhere can be checked against the fp64 logits of the
+ * experts it names.  An index outside [0, M) gives NaN.
+ */
+int oracle_logits_at(int dt, const void* X, int64_t N, int64_t h, const void* A, int64_t r,
+                     const void* B, int64_t M, const float* bias, int fullrank, int k,
+                     const int32_t* idx, double* out, int nthreads) {
+    if (dt < OR_DT_BF16 || dt > OR_DT_F64 || !X || !A || (!fullrank && !B) || !idx || !out) return OR_ERR_ARG;
+    if (N < 0 || h < 1 || M < 1 || (!fullrank && r < 1) || k < 1) return OR_ERR_ARG;
+    int T = 1;
+#ifdef _OPENMP
+    T = nthreads > 0 ? nthreads : omp_get_max_threads();
+#endif
+    (void)nthreads;
+    const size_t zr = (size_t)(r > 0 ? r : 1);
+    double* zs = (double*)malloc(sizeof(double) * (size_t)T * zr);
+    if (!zs) return OR_ERR_NOMEM;
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(T) schedule(static)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        int t = 0;
+#ifdef _OPENMP
+        t = omp_get_thread_num();
+#endif
+        double* z = zs + (size_t)t * zr;
+        if (!fullrank) {
+            /* z_j = sum_i x_i R1[i][j] */
+            for (int64_t j = 0; j < r; ++j) {
+                double s = 0.0;
+                for (int64_t i = 0; i < h; ++i) s += load_elem(dt, X, n * h + i) * load_elem(dt, A, i * r + j);
+                z[j] = s;
+            }
+        }
+        for (int c = 0; c < k; ++c) {
+            const int64_t m = idx[n * k + c];
+            if (m < 0 || m >= M) {
+                out[n * k + c] = NAN;
+                continue;
+            }
+            double s = 0.0;
+            if (fullrank) {
+                for (int64_t i = 0; i < h; ++i) s += load_elem(dt, X, n * h + i) * load_elem(dt, A, i * M + m);
+            } else {
+                for (int64_t j = 0; j < r; ++j) s += z[j] * load_elem(dt, B, j * M + m);
+            }
+            out[n * k + c] = s + (bias ? (double)bias[m] : 0.0);
+        }
+    }
+    free(zs);
+    return OR_OK;
+}
+
+/*
  * Column sums of the row-wise full softmax (eq. (6), (7)): psum[i] = sum_n
  * P_{n,i}.  Per token: logits as above, m = max l, Z = sum exp(l - m),
  * P = exp(l - m) / Z; each thread sums its tokens, the thread sums are added

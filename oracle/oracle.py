@@ -49,10 +49,11 @@ def _load():
         lib.oracle_route_fullrank.argtypes = [i32, p, i64, i64, p, i64, p, i32, i32,
                                               p, p, p, p, p, p, p, i32]
         lib.oracle_logits.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, p]
+        lib.oracle_logits_at.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, i32, p, p, i32]
         lib.oracle_softmax_colsum.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, p, i32]
         lib.oracle_backward_lowrank.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, i32, p, p, p,
                                                 p, p, p, p, i32]
-        for f in (lib.oracle_route_lowrank, lib.oracle_route_fullrank, lib.oracle_logits,
+        for f in (lib.oracle_route_lowrank, lib.oracle_route_fullrank, lib.oracle_logits, lib.oracle_logits_at,
                   lib.oracle_softmax_colsum, lib.oracle_backward_lowrank):
             f.restype = C.c_int
         lib.oracle_max_threads.restype = C.c_int
@@ -135,6 +136,30 @@ def logits(X, A, B, bias, fullrank: bool = False) -> np.ndarray:
     out = np.empty((N, M), np.float64)
     _check(_load().oracle_logits(dt, _ptr(X), N, h, _ptr(A), r, _ptr(None if fullrank else B), M,
                                  _ptr(b), int(fullrank), _ptr(out)))
+    return out
+
+
+def logits_at(X, A, B, bias, idx, fullrank: bool = False, nthreads: int = 0) -> np.ndarray:
+    """fp64 logits of the experts named by idx (N x k): out[n, j] = l[n, idx[n, j]]
+    with l = (x A) B + b, or x A + b when fullrank (A = W).  NaN where an
+    index lies outside [0, M)."""
+    X, A = np.ascontiguousarray(X), np.ascontiguousarray(A)
+    dt = _dt_code(X)
+    N, h = X.shape
+    if fullrank:
+        M, r = A.shape[1], 0
+    else:
+        B = np.ascontiguousarray(B)
+        r, M = B.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    assert idx.ndim == 2 and idx.shape[0] == N
+    k = idx.shape[1]
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty((N, k), np.float64)
+    if N == 0 or k == 0:
+        return out
+    _check(_load().oracle_logits_at(dt, _ptr(X), N, h, _ptr(A), r, _ptr(None if fullrank else B), M,
+                                    _ptr(b), int(fullrank), k, _ptr(idx), _ptr(out), nthreads))
     return out
 
 

@@ -18,3 +18,17 @@ def oracle_lib():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+_FULL_X = {}
+
+
+@pytest.fixture(scope="session")
+def full_tokens():
+    """full_tokens(cfg): the seeded X of a workload at its full N (generated once
+    per session; about 1 GiB for the headline)."""
+    def get(cfg):
+        if cfg.name not in _FULL_X:
+            _FULL_X[cfg.name] = cfg.x_rows(0)
+        return _FULL_X[cfg.name]
+    return get

@@ -31,7 +31,7 @@ from rank_router_top_amd import configs as CF
 from rank_router_top_amd import inputs as I
 from rank_router_top_amd import route as R
 
-from parity import compare, gap_clear
+from oracle.parity import compare, gap_clear
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -98,7 +98,8 @@ def check_balance(oracle_lib, X, R1, R2, b, k, gate, label, n_ws=None):
     g = run_balance(X, R1, R2, b, k, gate, n_ws)
     o = oracle_lib.balance_lowrank(X, R1, R2, b, k, gate)
     N = X.shape[0]
-    res = compare(o, g, k, gate == R.MORE_GATE_FULL_SOFTMAX, 2e-4, label)
+    at = oracle_lib.logits_at(X, R1, R2, b, g["idx"])
+    res = compare(o, g, k, gate == R.MORE_GATE_FULL_SOFTMAX, 2e-4, label, at)
     lerr = np.abs(g["lse"].astype(np.float64) - o["lse"])
     assert np.all(lerr <= 1e-4 * np.maximum(1.0, np.abs(o["lse"]))), f"{label}: lse off"
     check_psum(o["psum"], g["psum"], N, label)
@@ -200,31 +201,40 @@ def test_balance_rejects_outside_envelope():
 def test_balance_full_size_headline(oracle_lib):
     """Headline shape at full size (N = 262144, h = 2048, M = 4096, r = 32,
     k = 8, bias), in the launch configuration the benchmark times (workspace
-    for all N tokens).  The batch is 32 copies of one 8192-row block of the
-    seeded tokens, so the oracle on that block fixes the whole result:
-    psum = 32 x the block's psum, counts = 32 x the block's counts, L_bal and
-    H_norm equal the block's (both are invariant under repeating every
-    token); every copy of a row must give the same indices, gates and lse."""
+    for all N tokens).  The batch repeats one 8191-row block of the seeded
+    tokens (an odd period, so no copy lines up with the 32-token blocks or the
+    persistent grid's strides; the last copy is cut at N).  The oracle on that
+    block fixes the whole result: psum and counts are 32 x the block's plus
+    those of its first 32 rows, L_bal and H_norm follow from them; every copy
+    of a row must give the same indices, gates and lse."""
     cfg = CF.HEADLINE
-    base_n, reps = 8192, cfg.N // 8192
+    base_n = 8191
+    reps = -(-cfg.N // base_n)
+    tail = cfg.N - (reps - 1) * base_n
     Xb = cfg.x_rows(0, 0, base_n, n_total=cfg.N)
     R1, R2, b = cfg.weights(0)
     say("full size: oracle on the base block")
     o = oracle_lib.balance_lowrank(Xb, R1, R2, b, cfg.k, 0)
+    ot = oracle_lib.balance_lowrank(Xb[:tail], R1, R2, b, cfg.k, 0)
     say("full size: GPU on the tiled batch")
-    g = run_balance(np.tile(Xb, (reps, 1)), R1, R2, b, cfg.k, 0)
+    g = run_balance(np.tile(Xb, (reps, 1))[:cfg.N], R1, R2, b, cfg.k, 0)
     N = cfg.N
-    idx = g["idx"].reshape(reps, base_n, cfg.k)
-    gate = g["gate"].reshape(reps, base_n, cfg.k)
-    lse = g["lse"].reshape(reps, base_n)
-    for c in range(1, reps):
-        assert np.array_equal(idx[c], idx[0]) and np.array_equal(gate[c], gate[0]) and np.array_equal(lse[c], lse[0])
+    for key in ("idx", "gate", "lse", "logit"):
+        v = g[key]
+        for c in range(1, reps):
+            n0 = c * base_n
+            n1 = min(n0 + base_n, N)
+            assert np.array_equal(v[n0:n1], v[:n1 - n0]), f"copy {c} differs in {key}"
     first = {key: v[:base_n] for key, v in g.items() if key in ("idx", "gate", "logit", "lse")}
-    res = compare(o, first, cfg.k, False, 2e-4, "full-size block")
-    ps_o = reps * o["psum"]
+    res = compare(o, first, cfg.k, False, 2e-4, "full-size block", oracle_lib.logits_at(Xb, R1, R2, b, first["idx"]))
+    full_copies = reps - 1
+    ps_o = full_copies * o["psum"] + ot["psum"]
+    cnt_o = full_copies * o["counts"] + ot["counts"]
     check_psum(ps_o, g["psum"], N, "full-size")
-    diff = check_counts(reps * o["counts"], g["counts"], g["idx"], cfg.k, reps * res["excluded"], "full-size")
-    ob = dict(o, psum=ps_o)
+    excl_tail = int((~gap_clear(ot)).sum())
+    diff = check_counts(cnt_o, g["counts"], g["idx"], cfg.k, full_copies * res["excluded"] + excl_tail, "full-size")
+    lbal, hnorm = oracle_lib.balance_stats(ps_o, cnt_o, N, cfg.k)
+    ob = dict(o, psum=ps_o, counts=cnt_o, lbal=lbal, hnorm=hnorm)
     check_stats(ob, g, N, cfg.k, diff, "full-size")
     say(f"full size: ok {res} count moves {diff}")
 

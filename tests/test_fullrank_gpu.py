@@ -16,7 +16,7 @@ from rank_router_top_amd import configs as CF
 from rank_router_top_amd import inputs as I
 from rank_router_top_amd import route as R
 
-from parity import compare, gap_clear
+from oracle.parity import compare, gap_clear
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -69,7 +69,8 @@ def test_fullrank_shapes(oracle_lib, N, h, M, k, bias):
         say(f"N={N} h={h} M={M} k={k} bias={bias} gate={gate}")
         g = run(X, W, b, k, gate)
         o = oracle_lib.route_fullrank(X, W, b, k, gate)
-        say(f"ok {compare(o, g, k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, 'fullrank-shape')}")
+        at = oracle_lib.logits_at(X, W, None, b, g["idx"], fullrank=True)
+        say(f"ok {compare(o, g, k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, 'fullrank-shape', at)}")
 
 
 def test_fullrank_exact_ties(oracle_lib):
@@ -93,7 +94,8 @@ def test_fullrank_exact_ties(oracle_lib):
                 say(f"ties k={k} bias={b is not None} gate={gate}")
                 g = run(X, W, b, k, gate)
                 o = oracle_lib.route_fullrank(X, W, b, k, gate)
-                compare(o, g, k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, "fullrank-ties")
+                at = oracle_lib.logits_at(X, W, None, b, g["idx"], fullrank=True)
+                compare(o, g, k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, "fullrank-ties", at)
                 lo = o["logit"]
                 d = np.abs(np.diff(lo, axis=1)) if k > 1 else np.zeros((N, 0))
                 sep = np.all((d == 0) | (d > 1e-3), axis=1) & gap_clear(o)
@@ -140,4 +142,5 @@ def test_fullrank_full_size(oracle_lib, gate):
         v = g[key].reshape((reps, base_n) + g[key].shape[1:])
         assert all(np.array_equal(v[c], v[0]) for c in range(1, reps)), key
     first = {key: (None if v is None else v[:base_n]) for key, v in g.items()}
-    say(f"full size gate={gate}: ok {compare(o, first, cfg.k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, 'fullrank-full')}")
+    at = oracle_lib.logits_at(Xb, W, None, b, first["idx"], fullrank=True)
+    say(f"full size gate={gate}: ok {compare(o, first, cfg.k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, 'fullrank-full', at)}")

@@ -15,7 +15,7 @@ from rank_router_top_amd import configs as CF
 from rank_router_top_amd import inputs as I
 from rank_router_top_amd import route as R
 
-from parity import compare, gap_clear
+from oracle.parity import compare, gap_clear
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -62,7 +62,8 @@ def test_sharded_equals_full_route(oracle_lib, cfg, n, width, gate):
     say(f"{cfg.name} N={n} M={cfg.M} shard width {width} gate={gate}")
     g = sharded_route(X, R1, R2, b, cfg.k, gate, width)
     o = oracle_lib.route_lowrank(X, R1, R2, b, cfg.k, gate)
-    say(f"ok {compare(o, g, cfg.k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, 'sharded')}")
+    at = oracle_lib.logits_at(X, R1, R2, b, g["idx"])
+    say(f"ok {compare(o, g, cfg.k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, 'sharded', at)}")
 
 
 def test_sharded_ties_lower_index_wins(oracle_lib):
@@ -85,7 +86,8 @@ def test_sharded_ties_lower_index_wins(oracle_lib):
             say(f"ties k={k} gate={gate}")
             g = sharded_route(X, R1, R2, bf, k, gate, width)
             o = oracle_lib.route_lowrank(X, R1, R2, bf, k, gate)
-            compare(o, g, k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, "sharded-ties")
+            compare(o, g, k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, "sharded-ties",
+                    oracle_lib.logits_at(X, R1, R2, bf, g["idx"]))
             lo = o["logit"]
             d = np.abs(np.diff(lo, axis=1)) if k > 1 else np.zeros((N, 0))
             sep = np.all((d == 0) | (d > 1e-3), axis=1) & gap_clear(o)

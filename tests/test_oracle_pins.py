@@ -214,6 +214,90 @@ def test_hypercube_loads_within_bernstein_bound(oracle_lib):
     assert np.max(np.abs(loads - n * k / M)) <= bound
 
 
+# ------------------------------------- the gap rule's max|l|: hypercube closed form
+@pytest.mark.parametrize("r,shift", [(5, 0.0), (7, -0.75), (8, 1.25)])
+def test_maxabs_is_hypercube_closed_form(oracle_lib, r, shift):
+    """The gap rule scales by max_j |l_j| over all M experts of the token.
+    Under the hypercube router of Prop. 1 (experts = every sign vector a of
+    {+-1}^r, logit sum_l a_l z_l) the largest logit is sum_l |z_l| (a = sign z)
+    and the smallest is its negative (a = -sign z).  A constant bias c on every
+    expert moves both, so max_j |l_j| = sum_l |z_l| + |c| exactly (sums of a
+    few bf16 values are exact in fp64).  A maximum of l instead of |l|, or a
+    maximum over the selected experts only, gives sum|z| - |c| or less for
+    c != 0 or k small."""
+    h = 2 * r
+    R1, R2 = hypercube(r, h)
+    M = 2 ** r
+    X = I.make_x(r, 23, 96, h, I.DT_BF16, False)
+    b = None if shift == 0.0 else np.full(M, shift, np.float32)
+    got = oracle_lib.route_lowrank(X, I.f32_to_bf16_bits(R1), I.f32_to_bf16_bits(R2), b, 2)
+    z = I.to_f64(X, I.DT_BF16)[:, :r]
+    expect = np.abs(z).sum(axis=1) + abs(shift)
+    assert np.array_equal(got["maxabs"], expect)
+
+
+def test_maxabs_over_all_experts_random_rows(oracle_lib):
+    """max|l| is taken over every expert of the token, bias included: equal to
+    the largest magnitude in the token's full logit row (oracle_logits, pinned
+    separately by exact rationals and the low-rank = full-rank identity), on
+    rows where the most negative logit outweighs the largest."""
+    cfg = CF.HEADLINE
+    X = I.make_x(1, 24, 48, 128, I.DT_BF16, True)
+    R1 = I.make_r1(1, 24, 128, 16, I.DT_BF16)
+    R2 = I.make_r2(1, 24, 16, 300, I.DT_BF16)
+    b = (I.make_bias(1, 24, 300) - 2.0).astype(np.float32)     # mostly negative logits
+    full = oracle_lib.logits(X, R1, R2, b)
+    got = oracle_lib.route_lowrank(X, R1, R2, b, cfg.k)
+    assert np.array_equal(got["maxabs"], np.abs(full).max(axis=1))
+    assert np.any(-full.min(axis=1) > full.max(axis=1))         # the case |min| > max is exercised
+
+
+# ------------------------------------------ logits at given experts (the parity rule's gather)
+def test_logits_at_exact_rationals(oracle_lib):
+    """oracle_logits_at evaluates the logit definition at chosen experts: equal
+    to exact rational logits (x R1) R2 + b at those experts, low rank and full
+    rank; NaN for an index outside [0, M)."""
+    rng = np.random.default_rng(31)
+    h, r, M, N, k = 6, 3, 11, 5, 4
+    X = I.f32_to_bf16_bits(rng.standard_normal((N, h)).astype(np.float32))
+    R1 = I.f32_to_bf16_bits((rng.standard_normal((h, r)) / 2).astype(np.float32))
+    R2 = I.f32_to_bf16_bits(rng.standard_normal((r, M)).astype(np.float32))
+    b = (rng.standard_normal(M) * 0.3).astype(np.float32)
+    Xf, R1f, R2f = (I.bf16_bits_to_f32(a) for a in (X, R1, R2))
+    exact = frac_logits(Xf, R1f, R2f, b)
+    idx = rng.integers(0, M, (N, k)).astype(np.int32)
+    idx[1, 2] = M            # out of range
+    idx[3, 0] = -1
+    got = oracle_lib.logits_at(X, R1, R2, b, idx)
+    for n in range(N):
+        for j in range(k):
+            m = idx[n, j]
+            if 0 <= m < M:
+                assert got[n, j] == pytest.approx(float(exact[n][m]), rel=1e-14, abs=1e-14)
+            else:
+                assert np.isnan(got[n, j])
+    # full rank: x W + b with W = R1 R2 formed exactly (rational), stored in fp64
+    W = np.array([[float(sum(Fraction(float(R1f[i, q])) * Fraction(float(R2f[q, m])) for q in range(r)))
+                   for m in range(M)] for i in range(h)])
+    ok = np.clip(idx, 0, M - 1)
+    gf = oracle_lib.logits_at(I.to_f64(X, I.DT_BF16), W, None, b, ok, fullrank=True)
+    for n in range(N):
+        for j in range(k):
+            assert gf[n, j] == pytest.approx(float(exact[n][ok[n, j]]), rel=1e-12, abs=1e-12)
+
+
+def test_logits_at_agrees_with_route_outputs(oracle_lib):
+    """At the oracle's own selection, logits_at returns exactly the selected
+    logits that route_lowrank reports (two entry points, one definition)."""
+    X = I.make_x(2, 25, 64, 256, I.DT_BF16, True)
+    R1 = I.make_r1(2, 25, 256, 32, I.DT_BF16)
+    R2 = I.make_r2(2, 25, 32, 700, I.DT_BF16)
+    b = I.make_bias(2, 25, 700)
+    o = oracle_lib.route_lowrank(X, R1, R2, b, 8)
+    at = oracle_lib.logits_at(X, R1, R2, b, o["idx"])
+    assert np.array_equal(at, o["logit"])
+
+
 # ------------------------------------------------------ Lemma 3: relabelling equivariance
 def test_permuting_experts_permutes_indices(oracle_lib):
     """Lemma 3: relabelling the experts (columns of R2 together with the bias)

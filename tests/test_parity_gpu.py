@@ -16,7 +16,7 @@ from rank_router_top_amd import configs as CF
 from rank_router_top_amd import inputs as I
 from rank_router_top_amd import route as R
 
-from parity import compare, gap_clear
+from oracle.parity import compare, gap_clear, properties
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -51,7 +51,8 @@ def check_lowrank(oracle_lib, X, R1, R2, b, k, gate, label, logit_tol=2e-4):
     say(f"{label}: N={X.shape[0]} h={X.shape[1]} r={R1.shape[1]} M={R2.shape[1]} k={k} gate={gate}")
     g = run_lowrank(X, R1, R2, b, k, gate)
     o = oracle_lib.route_lowrank(X, R1, R2, b, k, gate)
-    res = compare(o, g, k, gate == R.MORE_GATE_FULL_SOFTMAX, logit_tol, label)
+    at = oracle_lib.logits_at(X, R1, R2, b, g["idx"])
+    res = compare(o, g, k, gate == R.MORE_GATE_FULL_SOFTMAX, logit_tol, label, at)
     say(f"{label}: ok {res}")
     return o, g
 
@@ -67,6 +68,7 @@ CASES = [
     (CF.RANK64, 1024 + 31, CF.GATE_TOPK_SOFTMAX),
     (CF.RANK128, 1024 + 64, CF.GATE_TOPK_SOFTMAX),
     (CF.MANY_DECODE, 256, CF.GATE_FULL_SOFTMAX),
+    (CF.MANY_PREFILL, 2048 + 19, CF.GATE_FULL_SOFTMAX),
 ]
 
 
@@ -94,7 +96,8 @@ def test_fullrank_baseline(oracle_lib, gate):
     say(f"fullrank: N={n} gate={gate}")
     g = run_fullrank(X, W, b, cfg.k, gate)
     o = oracle_lib.route_fullrank(X, W, b, cfg.k, gate)
-    say(f"fullrank: ok {compare(o, g, cfg.k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, 'fullrank')}")
+    at = oracle_lib.logits_at(X, W, None, b, g["idx"], fullrank=True)
+    say(f"fullrank: ok {compare(o, g, cfg.k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, 'fullrank', at)}")
 
 
 def test_fullrank_tiny_fp32(oracle_lib):
@@ -105,7 +108,7 @@ def test_fullrank_tiny_fp32(oracle_lib):
     say("fullrank fp32 tiny")
     g = run_fullrank(X, W, b, 5, 0)
     o = oracle_lib.route_fullrank(X, W, b, 5, 0)
-    compare(o, g, 5, False, 1e-5, "fullrank-f32")
+    compare(o, g, 5, False, 1e-5, "fullrank-f32", oracle_lib.logits_at(X, W, None, b, g["idx"], fullrank=True))
 
 
 # ------------------------------------------------------------------------ edge cases
@@ -208,7 +211,8 @@ def test_hypercube_router(oracle_lib):
     top1 = ((z > 0).astype(np.int64) << np.arange(r)).sum(1)
     assert np.array_equal(g["idx"][:, 0], top1.astype(np.int32))
     o = oracle_lib.route_lowrank(X, I.f32_to_bf16_bits(R1), I.f32_to_bf16_bits(R2), None, 4, 0)
-    compare(o, g, 4, False, 2e-4, "hypercube")
+    at = oracle_lib.logits_at(X, I.f32_to_bf16_bits(R1), I.f32_to_bf16_bits(R2), None, g["idx"])
+    compare(o, g, 4, False, 2e-4, "hypercube", at)
 
 
 def test_expert_permutation_equivariance():
@@ -284,7 +288,8 @@ def test_packed_workspace_sizes(oracle_lib):
             g = to_np(R.route_lowrank_packed(R.to_device(Xn, DEV), cfg.r, cfg.M, cfg.k, 0, ws))
             torch.cuda.synchronize()
             o = oracle_lib.route_lowrank(Xn, *cfg.weights(0), cfg.k, 0)
-            compare(o, g, cfg.k, False, 2e-4, f"packed-{n_ws}-{n}")
+            at = oracle_lib.logits_at(Xn, *cfg.weights(0), g["idx"])
+            compare(o, g, cfg.k, False, 2e-4, f"packed-{n_ws}-{n}", at)
 
 
 def test_ties_many_experts(oracle_lib):
@@ -306,7 +311,7 @@ def test_ties_many_experts(oracle_lib):
         say(f"ties M=4096 gate={gate}")
         g = run_lowrank(X, R1, R2, b, 8, gate)
         o = oracle_lib.route_lowrank(X, R1, R2, b, 8, gate)
-        compare(o, g, 8, gate == 1, 2e-4, "ties-4096")
+        compare(o, g, 8, gate == 1, 2e-4, "ties-4096", oracle_lib.logits_at(X, R1, R2, b, g["idx"]))
         # where the oracle's distinct logits are well separated, the full
         # ordered lists (ties included) must agree
         lo = o["logit"]
@@ -315,31 +320,68 @@ def test_ties_many_experts(oracle_lib):
         assert np.array_equal(g["idx"][sep], o["idx"][sep]), "tie rule violated"
 
 
-@pytest.mark.parametrize("gate", [CF.GATE_TOPK_SOFTMAX, CF.GATE_FULL_SOFTMAX])
-def test_headline_full_size(oracle_lib, gate):
-    """Headline workload at full size (N = 262144, h = 2048, M = 4096, r = 32,
-    k = 8, bias) in the launch configuration the benchmark times: weights
-    packed once, workspace for all N tokens (projection + routing kernels).
-    The batch is 32 copies of one 8192-row block of the seeded tokens: the
-    oracle checks the block, and every copy of a row must give bitwise the same
-    indices, gates and logits (rows are routed independently)."""
-    cfg = CF.HEADLINE
-    base_n, reps = 8192, cfg.N // 8192
-    Xb = cfg.x_rows(0, 0, base_n, n_total=cfg.N)
-    R1, R2, b = cfg.weights(0)
-    say(f"full size gate={gate}: oracle on the base block")
-    o = oracle_lib.route_lowrank(Xb, R1, R2, b, cfg.k, gate)
-    say(f"full size gate={gate}: GPU on the tiled batch")
-    X = R.to_device(np.tile(Xb, (reps, 1)), DEV)
-    d = [R.to_device(a, DEV) for a in (R1, R2, b)]
-    nbytes = R.workspace_bytes(False, R.MORE_DT_BF16, cfg.N, cfg.h, cfg.r, cfg.M, cfg.k, gate, True)
+def sample_rows(N, extra, seed):
+    """One row of every 32-token block (at a position that walks through the
+    block from one block to the next) plus `extra` seeded random rows."""
+    nb = (N + 31) // 32
+    per_block = np.minimum(np.arange(nb) * 32 + (np.arange(nb) * 13 + 5) % 32, N - 1)
+    rnd = np.random.default_rng(seed).choice(N, size=min(extra, N), replace=False)
+    return np.unique(np.concatenate([per_block, rnd]))
+
+
+def route_packed_full(X_np, cfg, gate):
+    """Route all rows of X in the launch configuration the benchmark times:
+    weights packed once, workspace for all N tokens."""
+    X = R.to_device(X_np, DEV)
+    d = [R.to_device(a, DEV) for a in cfg.weights(0)]
+    nbytes = R.workspace_bytes(False, R.MORE_DT_BF16, X_np.shape[0], cfg.h, cfg.r, cfg.M, cfg.k, gate,
+                               d[2] is not None)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     R.pack_lowrank(*d, ws)
     g = to_np(R.route_lowrank_packed(X, cfg.r, cfg.M, cfg.k, gate, ws))
     torch.cuda.synchronize()
-    for key in ("idx", "gate", "logit") + (("lse",) if gate else ()):
-        v = g[key].reshape((reps, base_n) + g[key].shape[1:])
-        assert all(np.array_equal(v[c], v[0]) for c in range(1, reps)), key
-    first = {key: (None if v is None else v[:base_n]) for key, v in g.items()}
-    res = compare(o, first, cfg.k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, "full-size")
+    return g
+
+
+@pytest.mark.parametrize("gate", [CF.GATE_TOPK_SOFTMAX, CF.GATE_FULL_SOFTMAX])
+def test_headline_full_size(oracle_lib, full_tokens, gate):
+    """Headline workload at full size (N = 262144 seeded tokens, h = 2048,
+    M = 4096, r = 32, k = 8, bias) in the launch configuration the benchmark
+    times.  Every row is checked for the properties that need no oracle; the
+    oracle checks one row of every 32-token block plus 8192 random rows, so an
+    error in which block a wave reads or writes shows up wherever it falls."""
+    cfg = CF.HEADLINE
+    say(f"full size gate={gate}: generating the {cfg.N} seeded tokens")
+    X = full_tokens(cfg)
+    say(f"full size gate={gate}: GPU on all tokens")
+    g = route_packed_full(X, cfg, gate)
+    properties(g, cfg.k, cfg.M, gate == CF.GATE_FULL_SOFTMAX, "full-size")
+    rows = sample_rows(cfg.N, 8192, 17)
+    R1, R2, b = cfg.weights(0)
+    say(f"full size gate={gate}: oracle on {rows.size} sampled rows")
+    o = oracle_lib.route_lowrank(X[rows], R1, R2, b, cfg.k, gate)
+    sub = {key: (None if v is None else v[rows]) for key, v in g.items()}
+    at = oracle_lib.logits_at(X[rows], R1, R2, b, sub["idx"])
+    res = compare(o, sub, cfg.k, gate == CF.GATE_FULL_SOFTMAX, 2e-4, "full-size", at)
     say(f"full size gate={gate}: ok {res}")
+
+
+def test_many_experts_prefill_full_size(oracle_lib, full_tokens):
+    """Many-expert prefill at full size (N = 65536, h = 4096, M = 65536, r = 64,
+    k = 16, full-softmax gate): enough 32-token blocks that every wave of the
+    persistent grid routes several of them.  Properties on every row; the
+    oracle on one row of every 8th block plus 512 random rows."""
+    cfg = CF.MANY_PREFILL
+    say("many-expert prefill full size: generating tokens")
+    X = full_tokens(cfg)
+    say("many-expert prefill full size: GPU on all tokens")
+    g = route_packed_full(X, cfg, CF.GATE_FULL_SOFTMAX)
+    properties(g, cfg.k, cfg.M, True, "many-prefill-full")
+    rows = np.unique(np.concatenate([sample_rows(cfg.N, 512, 23)[::8], [cfg.N - 1]]))
+    R1, R2, b = cfg.weights(0)
+    say(f"many-expert prefill full size: oracle on {rows.size} rows")
+    o = oracle_lib.route_lowrank(X[rows], R1, R2, b, cfg.k, CF.GATE_FULL_SOFTMAX)
+    sub = {key: (None if v is None else v[rows]) for key, v in g.items()}
+    at = oracle_lib.logits_at(X[rows], R1, R2, b, sub["idx"])
+    res = compare(o, sub, cfg.k, True, 2e-4, "many-prefill-full", at)
+    say(f"many-expert prefill full size: ok {res}")
