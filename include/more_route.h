@@ -81,7 +81,8 @@ typedef enum {
     MORE_ERR_WORKSPACE = 6,   /* workspace NULL/too small/misaligned             */
     MORE_ERR_UNSUPPORTED = 7, /* outside the envelope: h % 8, r % 16, r > 128    */
     MORE_ERR_HIP = 8,         /* a HIP launch or query failed                    */
-    MORE_ERR_ALIGNMENT = 9    /* a tensor pointer is not 16-byte aligned         */
+    MORE_ERR_ALIGNMENT = 9,   /* a tensor pointer is not 16-byte aligned         */
+    MORE_ERR_STALLED = 10     /* a kernel's bounded wait gave up: outputs invalid */
 } more_status;
 
 typedef enum {
@@ -158,9 +159,9 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
  *              weights, then the token scratch and the per-slot partial sums
  *              (overwritten).
  * Envelope: the shapes whose routing runs as the projection + routing
- * kernel pair: bf16, k <= 8, M <= 5888 (M <= 14720 for k <= 4), and R1 small
- * enough to stay in the projection kernel's LDS (h <= 4608 for r = 16,
- * h <= 2048 for r = 32, h <= 768 for r = 48 or 64); other shapes return
+ * kernel pair: bf16, k <= 8, M <= 65536, and R1 small enough to stay in the
+ * projection kernel's LDS (h <= 4608 for r = 16, h <= 2048 for r = 32,
+ * h <= 768 for r = 48 or 64); other shapes return
  * MORE_ERR_UNSUPPORTED (more_balance_workspace_bytes returns 0 for them).  psum, counts and stats are written in a fixed
  * summation order (the same inputs give the same bits).  N = 0 is a no-op.
  */
@@ -289,6 +290,40 @@ more_status more_route_fullrank(more_dtype dt, const void* X, int64_t N, int64_t
  */
 size_t more_route_workspace_bytes(int fullrank, more_dtype dt, int64_t N, int64_t h, int64_t r,
                                   int64_t M, int32_t k, more_gate gate, int has_bias);
+
+/*
+ * Testing aid: restrict the kernel forms the low-rank routing calls may take
+ * to a comma-separated subset of "split,pc,lock,stream" (the plain kernel,
+ * which fits every shape, always remains; an empty subset such as "none"
+ * leaves only it).  NULL or "" allows every form again.  Every form computes
+ * the same selection and gates; this only lets tests check each of them on
+ * shapes a faster one would take.  The environment variable MORE_ROUTE_PATHS
+ * sets the initial subset, read once at the first routing call.  Process-wide;
+ * not to be called while routing calls are being enqueued on other threads.
+ */
+void more_set_route_paths(const char* names);
+
+/*
+ * Outcome of the routing calls enqueued so far on a workspace.  The persistent
+ * routing kernels hand work between their waves through bounded waits; a wait
+ * that gives up (a protocol failure, never expected) makes every wave of that
+ * launch exit normally and records the failure in a status word at offset 0 of
+ * the workspace, which more_lowrank_pack clears.  This call synchronises
+ * `stream`, reads the word and clears it: MORE_OK, or MORE_ERR_STALLED when
+ * some routing, balancing or backward call on this workspace since the last
+ * check (or the last pack) returned invalid outputs.  MORE_ERR_NULL_ARG /
+ * MORE_ERR_WORKSPACE for a NULL or misaligned workspace, MORE_ERR_HIP if the
+ * synchronisation or a copy fails.  Host function.
+ */
+more_status more_route_status(void* workspace, void* stream);
+
+/*
+ * Testing aid: polls before a bounded wait gives up (<= 0 restores the
+ * default, 4194304).  Process-wide; a tiny value makes the waits give up from
+ * the host side so that the error path can be exercised without a failure on
+ * the device (every kernel still exits normally).
+ */
+void more_set_spin_limit(int polls);
 
 /* Static string for a status code (never NULL). */
 const char* more_status_str(more_status s);

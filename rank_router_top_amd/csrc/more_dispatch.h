@@ -6,8 +6,8 @@
 #include "more_stream.h"
 #include "more_lock.h"
 #include "more_pc.h"
-#include "more_slice.h"
 #include "more_split.h"
+#include "more_sweep.h"
 
 namespace more {
 
@@ -71,22 +71,20 @@ inline void proj_ksteps(long long h, int r16, int* ksp, bool* tail) {
   *ksp = (int)((ks + D - 1) / D * D);
 }
 constexpr bool split_shape_ok(int kmax, int r16, long long mpad) {
-  return kmax <= 8 && r16 <= 4 && mpad <= 65535;
+  return kmax <= 8 && r16 <= 4 && mpad <= 65536;   // 16-bit sweep positions
 }
 proj_fn pick_proj(int r16, bool tail);
 // lse: pass 1 over every tile and lse written (the full-softmax gate implies it).
 route_fn pick_route(bool full, bool lse, int kmax, int r16);
 size_t route_lds_bytes(int kmax, long long mpad);
 size_t proj_lds_bytes(int r16, int ksp);
+// Expert sweep with the up-projection tiles shared through LDS (the routing
+// half of the two-kernel form): bf16, k <= 8, r <= 64, M <= 65536.
+typedef void (*sweep_fn)(SweepArgs);
+constexpr int kSwCons = 8;   // consumer waves (+1 loader), one workgroup per CU
+sweep_fn pick_sweep(bool full, bool lse, int kmax, int r16);
+size_t sweep_lds_bytes(int kmax, int r16);
 
-// Expert-slice kernel: bf16, r in {16, 32}, M = 4096 (128 tiles), k <= 8.
-// LDS bytes (0: no instance) and instance.
-typedef void (*slice_fn)(SlArgs);
-constexpr bool slice_shape_ok(int kmax, int r16, long long mpad) {
-  return kmax <= kSlK && (r16 == 1 || r16 == 2) && mpad == (long long)kSlNT * kTile;
-}
-size_t slice_lds_bytes(bool full, int r16);
-slice_fn pick_slice(bool full, int r16, bool tail);
 
 lowrank_fn pick_lowrank_bf16_topk(int kmax, int r16);
 lowrank_fn pick_lowrank_bf16_full(int kmax, int r16);

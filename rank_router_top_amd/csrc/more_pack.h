@@ -5,17 +5,16 @@
 // caller's workspace (L2-resident: 128 KiB + 256 KiB at h=2048, r=32, M=4096).
 //
 // Sweep order.  Without a bias the experts are swept in index order.  With a
-// bias they are swept by bias descending (ties by index): experts with a large
-// bias tend to end in the top-k, so the running k-th value rises early and
-// fewer later logits pass the filter.  The selected set and its order do not
-// depend on the sweep order (ties are resolved by expert index at the end),
-// so this is purely a speed choice.
+// bias (M <= 16384) they are swept by bias descending (ties by index), as
+// sorted by more_order.h before this kernel runs: experts with a large bias tend to end
+// in the top-k, so the running k-th value rises early and fewer later logits
+// pass the filter.  The selected set and its order do not depend on the sweep
+// order (ties are resolved by expert index at the end), so this is purely a
+// speed choice.
 #pragma once
 #include "more_device.h"
 
 namespace more {
-
-constexpr int kPackLdsM = 16384;   // largest M whose bias the sweep-order blocks stage in LDS
 
 // Position p of the sweep holds expert perm[p] (perm[p] = -1 on the padding
 // positions M..M_pad-1).  Row i of tile t is position 32t + i.  For a lane of
@@ -32,7 +31,7 @@ struct PackArgs {
   int ksteps2;        // MFMA K-steps of the second product
   int ksteps1, rb;    // first product: K-steps over h and 32-row blocks of z (low rank only)
   int natural_k;      // 1: second-product K rows in memory order (full rank: the X operand)
-  int rank_blocks;    // blocks computing the sweep order (64 experts each)
+  int rank_blocks;    // blocks packing the second product's operands (64 sweep positions each)
   int r1_blocks;      // blocks packing R1
   int ksq, r16;       // producer layout of R1: 32-column K-steps (padded) and 16-rank blocks
   int r1q_blocks;     // blocks packing R1q (0: not wanted)
@@ -42,7 +41,9 @@ struct PackArgs {
   void* R2p;
   float* biasp;       // [NT][2][16] fp32, accumulator layout (fp32 kernels)
   uint32_t* biasq;    // [NT][64] bf16 pairs (hi, lo) as an MFMA A operand (bf16 kernels)
-  int* perm;          // [Mpad]
+  int* perm;          // [Mpad]: read (with a bias: sorted beforehand) or written (without)
+  float* colnorm2;    // [Mpad] or null: squared norm of the packed column at each sweep position
+  int sorted;         // 1: perm was written by order_count_kernel (bias-descending order)
 };
 
 // Element type helpers.
@@ -71,68 +72,50 @@ __global__ __launch_bounds__(1024) void pack_kernel(PackArgs a) {
   constexpr int EPL = (DT == 0) ? 8 : 1;          // elements per lane per K-step
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < a.rank_blocks) {
-    // ---- sweep order: rank of expert j by (bias desc, index asc); padding last
-    __shared__ int part[16][64];
-    __shared__ float4 bsh[kPackLdsM / 4];   // the bias, when it fits (read by broadcast)
-    const int jl = tid & 63, slice = tid >> 6;   // 64 experts x 16 slices
-    const int j = blockIdx.x * 64 + jl;
-    int cnt = 0;
-    if (a.bias && a.M <= kPackLdsM && (a.M & 3) == 0) {
-      for (int i = tid; i < a.M / 4; i += 1024) bsh[i] = ((const float4*)a.bias)[i];
-      __syncthreads();
-      if (j < a.M) {
-        const float bj = a.bias[j];
-        // slice s compares against experts 4q .. 4q+3 for q = s, s + 16, ... (all
-        // 64 lanes of a wave read the same float4)
-        for (int q = slice; q < a.M / 4; q += 16) {
-          const float4 b4 = bsh[q];
-          const int i = 4 * q;
-          cnt += (b4.x > bj) || (b4.x == bj && i < j);
-          cnt += (b4.y > bj) || (b4.y == bj && i + 1 < j);
-          cnt += (b4.z > bj) || (b4.z == bj && i + 2 < j);
-          cnt += (b4.w > bj) || (b4.w == bj && i + 3 < j);
-        }
-      }
-    } else if (a.bias && j < a.M) {
-      const float bj = a.bias[j];
-      const int per = (a.M + 15) / 16;
-      const int i0 = slice * per, i1 = min(a.M, i0 + per);
-      for (int i = i0; i < i1; ++i) {
-        const float bi = a.bias[i];
-        cnt += (bi > bj) || (bi == bj && i < j);
-      }
-    }
-    part[slice][jl] = cnt;
-    __syncthreads();
-    if (j >= a.Mpad) return;
-    int pos;
-    if (a.bias && j < a.M) {
-      pos = 0;
-      for (int s = 0; s < 16; ++s) pos += part[s][jl];
-    } else {
-      pos = j;
-    }
+    // ---- sweep position pos holds expert j = perm[pos] (sorted by
+    // order_count_kernel with a bias; index order otherwise); padding last
+    const int jl = tid & 63, slice = tid >> 6;   // 64 positions x 16 slices
+    // Mpad is a multiple of 64, so every position of the block is real (no
+    // early exit before the barrier below)
+    const int pos = blockIdx.x * 64 + jl;
+    const int j = a.sorted ? a.perm[pos] : (pos < a.M ? pos : -1);
     const int t = pos >> 5, i = pos & 31;
     const T* B = (const T*)a.R2;
     T* Bp = (T*)a.R2p;
-    // scatter column j of R2 (or W) into the packed tile at row i
+    // gather column j of R2 (or W) into the packed tile at row i
+    float sq = 0.f;
     for (int w = slice; w < a.ksteps2 * 2 * EPL; w += 16) {
       const int m = w / (2 * EPL), hf = (w / EPL) & 1, e = w % EPL;
       const int kr = k_row<DT>(m, e, hf, a.natural_k);
       T val = 0;
-      if (j < a.M && kr < a.kdim) val = B[(size_t)kr * a.M + j];
+      if (j >= 0 && kr < a.kdim) val = B[(size_t)kr * a.M + j];
       Bp[(((size_t)t * a.ksteps2 + m) * kWave + i + 32 * hf) * EPL + e] = val;
+      float f;
+      if constexpr (DT == 0) f = __uint_as_float((uint32_t)val << 16);
+      else f = (float)val;
+      sq = __builtin_fmaf(f, f, sq);
+    }
+    if (a.colnorm2) {
+      // the 16 slices' partial sums of squares -> the column's squared norm
+      __shared__ float part[16][64];
+      part[slice][jl] = sq;
+      __syncthreads();
+      if (slice == 0) {
+        float t2 = 0.f;
+        for (int q = 0; q < 16; ++q) t2 += part[q][jl];
+        a.colnorm2[pos] = t2;
+      }
     }
     if (slice == 0) {
-      a.perm[pos] = (j < a.M) ? j : -1;
+      if (!a.sorted) a.perm[pos] = j;
       const int hf = (i >> 2) & 1, v = 4 * (i >> 3) + (i & 3);
-      const float bv = (j < a.M) ? (a.bias ? a.bias[j] : 0.f) : -__builtin_inff();
+      const float bv = (j >= 0) ? (a.bias ? a.bias[j] : 0.f) : -__builtin_inff();
       a.biasp[(t * 2 + hf) * 16 + v] = bv;
       if (a.biasq) {
         // bias of row i as bf16 hi + lo in K-slots 0 and 1 of lane i (lanes 32..63
         // carry zeros): one MFMA against a ones operand adds hi + lo to every token.
         const bf16 bh = (bf16)bv;
-        const float rest = (j < a.M) ? bv - (float)bh : 0.f;
+        const float rest = (j >= 0) ? bv - (float)bh : 0.f;
         const bf16 bl = (bf16)rest;
         a.biasq[(size_t)t * kWave + i] =
             (uint32_t)__builtin_bit_cast(uint16_t, bh) | ((uint32_t)__builtin_bit_cast(uint16_t, bl) << 16);

@@ -67,6 +67,7 @@ struct PcArgs {
   int KSP;             // 32-column K-steps, padded to a multiple of D (zero R1 rows)
   int spin_limit;      // polls before a wait gives up
   int pre;             // seed-pass tiles: a multiple of 4 in [4, NT]
+  int* status;         // device word set to a nonzero code if a bounded wait gave up
 };
 
 // Hand-off counters (ints at the start of LDS)
@@ -462,6 +463,10 @@ __global__ __launch_bounds__(64 * kPcWaves) void pc_kernel(PcArgs pa) {
                             wave, lane, nbw);
   else
     pc_consume<KMAX, FULL, R16>(pa, pc_lds, wave - kPcProd, lane, nbw, has_bias);
+  // a wave whose bounded wait gave up (or saw another give up) reports it
+  asm volatile("" ::: "memory");
+  if (pa.status && __builtin_amdgcn_readfirstlane(pc_flags(pc_lds)[kPcAbort]) != 0)
+    __hip_atomic_store(pa.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace more

@@ -14,10 +14,12 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "more_route.h"
 #include "more_device.h"
 #include "more_pack.h"
+#include "more_order.h"
 #include "more_dispatch.h"
 #include "more_fullrank_tiled.h"
 #include "more_merge.h"
@@ -39,7 +41,7 @@ size_t log_bytes(int kmax) { return (size_t)(2 * kmax + 8) * kWave * sizeof(floa
 
 struct Layout {
   int NT, Mpad, r16, rb, ks1, ks2, ksq, epl, esize;
-  size_t off_r1p, off_r2p, off_bias, off_biasq, off_perm, off_r1q, total;
+  size_t off_status, off_r1p, off_r2p, off_bias, off_biasq, off_perm, off_r1q, off_colnorm, off_bmin, off_wstat, total;
 };
 
 // Workspace layout of one call.  All offsets are 256-byte aligned.
@@ -74,6 +76,9 @@ bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, L
     }
   }
   size_t off = 0;
+  // the stall word of the routing kernels' bounded waits (fixed place: offset 0)
+  L->off_status = off;
+  off += kAlign;
   L->off_r1p = off;
   off += align_up((size_t)L->ks1 * L->rb * lane_bytes);
   L->off_r2p = off;
@@ -87,6 +92,13 @@ bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, L
   off += align_up((size_t)L->Mpad * sizeof(int));
   L->off_r1q = off;
   off += align_up((size_t)L->ksq * L->r16 * 1024);
+  // weight statistics of the sweep kernel's error bound and seed pass
+  L->off_colnorm = off;
+  off += align_up((size_t)L->Mpad * sizeof(float));
+  L->off_bmin = off;
+  off += align_up((size_t)L->NT * sizeof(float));
+  L->off_wstat = off;
+  off += kAlign;
   L->total = off;
   return true;
 }
@@ -135,25 +147,40 @@ more_status validate(int fullrank, more_dtype dt, const void* X, int64_t N, int6
 // ---------------------------------------------------------------- dispatch
 // Kernel paths of the low-rank router, in the order they are tried (measured
 // fastest first on the workloads they share).  Each call takes the first one
-// whose shape envelope fits.  MORE_ROUTE_PATHS (environment, read at
-// every call) can restrict the candidates to a comma-separated subset of
-// "pc,slice,lock,stream,simple" -- a testing aid so that every path can be
-// checked on the shapes a faster one would take; "simple" always fits.
-enum { kPathPc = 1, kPathSlice = 2, kPathLock = 4, kPathStream = 8, kPathSplit = 16 };
-bool path_allowed(int path) {
-  const char* env = getenv("MORE_ROUTE_PATHS");
-  if (!env || !*env) return true;
-  const char* name = path == kPathSlice ? "slice" : path == kPathPc ? "pc" : path == kPathLock ? "lock"
-                     : path == kPathSplit ? "split" : "stream";
-  const size_t len = strlen(name);
-  for (const char* p = env; *p;) {
+// whose shape envelope fits.  A testing aid can restrict the candidates to a
+// subset of "split,pc,lock,stream" (the plain kernel always remains, so that
+// every path can be checked on the shapes a faster one would take): the
+// environment variable MORE_ROUTE_PATHS, read once at the first routing call,
+// or more_set_route_paths() at any time.
+enum { kPathPc = 1, kPathLock = 4, kPathStream = 8, kPathSplit = 16, kPathAll = 31 };
+
+int parse_paths(const char* names) {
+  if (!names || !*names) return kPathAll;
+  int mask = 0;
+  static const struct { const char* name; int bit; } table[] = {
+      {"split", kPathSplit}, {"pc", kPathPc}, {"lock", kPathLock}, {"stream", kPathStream}};
+  for (const char* p = names; *p;) {
     const char* e = strchr(p, ',');
     const size_t n = e ? (size_t)(e - p) : strlen(p);
-    if (n == len && strncmp(p, name, len) == 0) return true;
+    for (const auto& t : table)
+      if (n == strlen(t.name) && strncmp(p, t.name, n) == 0) mask |= t.bit;
     if (!e) break;
     p = e + 1;
   }
-  return false;
+  return mask;
+}
+
+std::atomic<int> g_paths{-1};   // -1: not read from the environment yet
+std::atomic<int> g_spin_limit{1 << 22};   // polls before a kernel's bounded wait gives up
+
+bool path_allowed(int path) {
+  int m = g_paths.load(std::memory_order_relaxed);
+  if (m < 0) {
+    int fresh = parse_paths(getenv("MORE_ROUTE_PATHS"));
+    g_paths.compare_exchange_strong(m, fresh);
+    m = g_paths.load(std::memory_order_relaxed);
+  }
+  return (m & path) != 0;
 }
 
 // Whether the two-kernel path has an instance for this shape (LDS included).
@@ -162,7 +189,7 @@ bool split_fits(int kmax, const Layout& L, int64_t h) {
   int ksp = 0;
   bool tail = false;
   proj_ksteps(h, L.r16, &ksp, &tail);
-  return (long long)proj_lds_bytes(L.r16, ksp) <= kLdsBytes && (long long)route_lds_bytes(kmax, L.Mpad) <= kLdsBytes;
+  return (long long)proj_lds_bytes(L.r16, ksp) <= kLdsBytes && (long long)sweep_lds_bytes(kmax, L.r16) <= kLdsBytes;
 }
 
 // Two kernels: projection (R1 resident in LDS) writes z of every 32-token
@@ -174,14 +201,14 @@ more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int k
   bool tail = false;
   proj_ksteps(h, L.r16, &ksp, &tail);
   const size_t pj_lds = proj_lds_bytes(L.r16, ksp);
-  const size_t rt_lds = route_lds_bytes(kmax, L.Mpad);
+  const size_t sw_lds = sweep_lds_bytes(kmax, L.r16);
   proj_fn pf = pick_proj(L.r16, tail);
-  route_fn rf = pick_route(full, lse_mode, kmax, L.r16);
+  sweep_fn sf = pick_sweep(full, lse_mode, kmax, L.r16);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipFuncSetAttribute((const void*)pf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pj_lds) != hipSuccess ||
-      hipFuncSetAttribute((const void*)rf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rt_lds) != hipSuccess)
+      hipFuncSetAttribute((const void*)sf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sw_lds) != hipSuccess)
     return MORE_ERR_HIP;
   const int64_t nb = (a.N + kTile - 1) / kTile;
   if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
@@ -194,17 +221,32 @@ more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int k
   pa.KSP = ksp;
   pa.NB = (int)nb;
   pa.Z = ws + L.total;
-  pa.spin_limit = 1 << 22;
+  pa.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  pa.status = (int*)(ws + L.off_status);
   const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kProjWaves - 1) / kProjWaves));
   hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, stream, pa);
   if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
-  RouteArgs ra;
-  ra.base = a;
-  ra.Z = pa.Z;
-  ra.NB = (int)nb;
-  ra.pre = std::min(L.NT, kPcSeedTiles);
-  const int64_t rg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kRouteWaves - 1) / kRouteWaves));
-  hipLaunchKernelGGL(rf, dim3((unsigned)rg), dim3(64 * kRouteWaves), rt_lds, stream, ra);
+  SweepArgs sa;
+  sa.Z = pa.Z;
+  sa.R2p = a.R2p;
+  sa.biasq = a.biasq;
+  sa.bmin = (const float*)(ws + L.off_bmin);
+  sa.wstat = (const float*)(ws + L.off_wstat);
+  sa.perm = a.perm;
+  sa.N = a.N;
+  sa.NB = (int)nb;
+  sa.NT = L.NT;
+  sa.k = a.k;
+  sa.out_idx = a.out_idx;
+  sa.out_gate = a.out_gate;
+  sa.out_logit = a.out_logit;
+  sa.out_lse = lse_mode ? a.out_lse : nullptr;
+  sa.status = pa.status;
+  sa.spin_limit = pa.spin_limit;
+  const int64_t sg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kSwCons - 1) / kSwCons));
+  // the loader's sequence (rounds x (seed + sweep) tiles) must fit an int
+  if ((nb / (sg * kSwCons) + 1) * 2 * (int64_t)L.NT >= ((int64_t)1 << 30)) return MORE_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(sf, dim3((unsigned)sg), dim3(64 * (kSwCons + 1)), sw_lds, stream, sa);
   return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 
@@ -254,11 +296,37 @@ more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* 
   p.biasp = (float*)(ws + L.off_bias);
   p.biasq = (uint32_t*)(ws + L.off_biasq);
   p.perm = (int*)(ws + L.off_perm);
+  p.colnorm2 = (float*)(ws + L.off_colnorm);
+  const bool ordered = bias && M <= kOrderMaxM;
+  if (ordered) {
+    // sweep order: experts by (bias desc, index asc)
+    OrderArgs o;
+    o.bias = bias;
+    o.M = (int)M;
+    o.Mpad = L.Mpad;
+    o.perm = p.perm;
+    hipLaunchKernelGGL(order_count_kernel, dim3((L.Mpad + 15) / 16), dim3(256), 0, stream, o);
+    if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
+  }
+  p.sorted = ordered ? 1 : 0;
   const int blocks = p.rank_blocks + p.r1_blocks + p.r1q_blocks;
   if (dt == MORE_DT_BF16)
     hipLaunchKernelGGL(pack_kernel<0>, dim3(blocks), dim3(1024), 0, stream, p);
   else
     hipLaunchKernelGGL(pack_kernel<1>, dim3(blocks), dim3(1024), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
+  TileStatArgs ts;
+  ts.bias = bias;
+  ts.perm = p.perm;
+  ts.colnorm2 = p.colnorm2;
+  ts.Mpad = L.Mpad;
+  ts.NT = L.NT;
+  ts.ordered = ordered ? 1 : 0;
+  ts.seed_tiles = std::min(L.NT, kPcSeedTiles);
+  ts.bmin = (float*)(ws + L.off_bmin);
+  ts.wstat = (float*)(ws + L.off_wstat);
+  ts.status = (int*)(ws + L.off_status);
+  hipLaunchKernelGGL(tilestat_kernel, dim3(1), dim3(1024), 0, stream, ts);
   return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 
@@ -267,6 +335,25 @@ more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* 
 extern "C" {
 
 int more_abi_version(void) { return MORE_ABI_VERSION; }
+
+void more_set_route_paths(const char* names) { g_paths.store(parse_paths(names), std::memory_order_relaxed); }
+
+void more_set_spin_limit(int polls) {
+  g_spin_limit.store(polls > 0 ? polls : (1 << 22), std::memory_order_relaxed);
+}
+
+more_status more_route_status(void* workspace, void* stream) {
+  if (!workspace) return MORE_ERR_NULL_ARG;
+  if (((uintptr_t)workspace % kAlign) != 0) return MORE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  int word = 0;
+  if (hipStreamSynchronize(s) != hipSuccess) return MORE_ERR_HIP;
+  if (hipMemcpy(&word, workspace, sizeof word, hipMemcpyDeviceToHost) != hipSuccess) return MORE_ERR_HIP;
+  if (word == 0) return MORE_OK;
+  const int zero = 0;
+  if (hipMemcpy(workspace, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) return MORE_ERR_HIP;
+  return MORE_ERR_STALLED;
+}
 
 const char* more_status_str(more_status s) {
   switch (s) {
@@ -280,6 +367,7 @@ const char* more_status_str(more_status s) {
     case MORE_ERR_UNSUPPORTED: return "unsupported shape (need h % 8 == 0, r % 16 == 0, r <= 128)";
     case MORE_ERR_HIP: return "HIP launch failed";
     case MORE_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case MORE_ERR_STALLED: return "a routing kernel's bounded wait gave up (outputs invalid)";
   }
   return "unknown status";
 }
@@ -371,35 +459,10 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
     pa.G = (int)std::max<int64_t>(1, std::min<int64_t>(cus, nb));
     pa.KSP = L.ksq;
     pa.R1q = ws + L.off_r1q;
-    pa.spin_limit = 1 << 22;
+    pa.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    pa.status = (int*)(ws + L.off_status);
     pa.pre = std::min(L.NT, kPcSeedTiles);
     hipLaunchKernelGGL(fn, dim3((unsigned)pa.G), dim3(64 * kPcWaves), pc_lds, (hipStream_t)stream, pa);
-    return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
-  }
-  const size_t sl_lds = (dt == MORE_DT_BF16 && L.ksq > 0 && slice_shape_ok(kmax, L.r16, L.Mpad))
-                            ? slice_lds_bytes(full, L.r16) : 0;
-  if (sl_lds > 0 && (long long)sl_lds <= kLdsBytes && path_allowed(kPathSlice)) {
-    // Expert-slice kernel: one 12-wave workgroup per CU, persistent.
-    int ksp = 0;
-    bool tail = false;
-    pc_ksteps(h, L.r16, &ksp, &tail);
-    slice_fn fn = pick_slice(full, L.r16, tail);
-    int dev = 0, cus = 0;
-    if (!fn || hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sl_lds) !=
-            hipSuccess)
-      return MORE_ERR_HIP;
-    SlArgs sa;
-    sa.base = a;
-    const int64_t nb = (N + kTile - 1) / kTile;
-    if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
-    sa.NB = (int)nb;
-    sa.G = (int)std::max<int64_t>(1, std::min<int64_t>(cus, nb));
-    sa.KSP = L.ksq;
-    sa.R1q = ws + L.off_r1q;
-    sa.spin_limit = 1 << 22;
-    hipLaunchKernelGGL(fn, dim3((unsigned)sa.G), dim3(64 * kSlWaves), sl_lds, (hipStream_t)stream, sa);
     return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
   }
   if (dt == MORE_DT_BF16 && lock_supported(kmax, L.r16, L.Mpad) && path_allowed(kPathLock)) {
@@ -659,7 +722,8 @@ more_status more_lowrank_backward_packed(more_dtype dt, const void* X, int64_t N
   pa.KSP = ksp;
   pa.NB = (int)nb;
   pa.Z = ws + B.off_z;
-  pa.spin_limit = 1 << 22;
+  pa.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  pa.status = (int*)(ws + L.off_status);
   const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kProjWaves - 1) / kProjWaves));
   hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, hs, pa);
   if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;

@@ -52,6 +52,7 @@ struct ProjArgs {
   int NB;            // 32-token blocks
   void* Z;           // [NB][hi, lo][R16][64 lanes][16 B]
   int spin_limit;    // polls before a wait gives up
+  int* status;       // device word set to a nonzero code if a bounded wait gave up
 };
 
 // z bytes of one 32-token block.
@@ -139,6 +140,7 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
       } else {
         if (__builtin_amdgcn_readfirstlane(*abort_word) != 0 || ++idle > pa.spin_limit) {
           *abort_word = 1;
+          if (pa.status) __hip_atomic_store(pa.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -228,7 +230,10 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
     // the 32x32x16 B-operand layout: lane 16g + l16 + 32(q4&1), elements
     // 4(q4>>1) .. +3 of K-step rb; into the slot once the writer has read the
     // previous block out of it
-    if (!pc_wait(freed + wave, jj, abort_word, pa.spin_limit)) return;
+    if (!pc_wait(freed + wave, jj, abort_word, pa.spin_limit)) {
+      if (pa.status) __hip_atomic_store(pa.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int off = (16 * g + l16 + 32 * (q4 & 1)) * 16 + 8 * (q4 >> 1);

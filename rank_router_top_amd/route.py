@@ -21,12 +21,13 @@ MORE_ERR_WORKSPACE = 6
 MORE_ERR_UNSUPPORTED = 7
 STATUS_NAMES = {0: "MORE_OK", 1: "MORE_ERR_NULL_ARG", 2: "MORE_ERR_BAD_SHAPE", 3: "MORE_ERR_BAD_K",
                 4: "MORE_ERR_BAD_DTYPE", 5: "MORE_ERR_BAD_GATE", 6: "MORE_ERR_WORKSPACE",
-                7: "MORE_ERR_UNSUPPORTED", 8: "MORE_ERR_HIP", 9: "MORE_ERR_ALIGNMENT"}
+                7: "MORE_ERR_UNSUPPORTED", 8: "MORE_ERR_HIP", 9: "MORE_ERR_ALIGNMENT", 10: "MORE_ERR_STALLED"}
+MORE_ERR_STALLED = 10
 EXPORTS = ("more_route_lowrank", "more_route_fullrank", "more_route_workspace_bytes",
            "more_status_str", "more_abi_version", "more_lowrank_pack", "more_lowrank_route_packed",
            "more_lowrank_balance_packed", "more_balance_workspace_bytes", "more_dispatch_sort",
            "more_dispatch_workspace_bytes", "more_lowrank_backward_packed", "more_backward_workspace_bytes",
-           "more_topk_merge")
+           "more_topk_merge", "more_set_route_paths", "more_route_status", "more_set_spin_limit")
 
 _lock = threading.Lock()
 _lib = None
@@ -82,6 +83,34 @@ def lib() -> C.CDLL:
             L.more_abi_version.restype = C.c_int
             _lib = L
     return _lib
+
+
+def set_route_paths(names: str | None) -> None:
+    """more_set_route_paths: restrict the kernel forms (testing aid; None = all)."""
+    L = lib()
+    L.more_set_route_paths.argtypes = [C.c_char_p]
+    L.more_set_route_paths.restype = None
+    L.more_set_route_paths(None if names is None else names.encode())
+
+
+def set_spin_limit(polls: int) -> None:
+    """more_set_spin_limit: polls before a kernel's bounded wait gives up (testing aid; 0 = default)."""
+    L = lib()
+    L.more_set_spin_limit.argtypes = [C.c_int]
+    L.more_set_spin_limit.restype = None
+    L.more_set_spin_limit(int(polls))
+
+
+def route_status(workspace, stream=None) -> int:
+    """more_route_status: synchronise the stream, read and clear the workspace's stall word.
+    Returns MORE_OK or MORE_ERR_STALLED (other codes raise)."""
+    L = lib()
+    L.more_route_status.argtypes = [C.c_void_p, C.c_void_p]
+    L.more_route_status.restype = C.c_int
+    code = L.more_route_status(_ptr(workspace), _stream(stream))
+    if code not in (MORE_OK, MORE_ERR_STALLED):
+        _check("more_route_status", code)
+    return code
 
 
 def status_str(code: int) -> str:

@@ -132,7 +132,7 @@ def call_balance(dt=0, N=64, h=256, r=32, M=4096, k=8, gate=0, idx=FAKE, g=FAKE,
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(k=16), 7), (dict(r=128), 7), (dict(dt=1), 7), (dict(M=6000), 7), (dict(M=14721, k=4), 7), (dict(M=14720, k=4, ws_bytes=100), 6),
+    (dict(k=16), 7), (dict(r=128), 7), (dict(dt=1), 7), (dict(M=65537), 7), (dict(M=65537, k=4), 7), (dict(M=14720, k=4, ws_bytes=100), 6),
     (dict(lse=None), 1), (dict(psum=None), 1), (dict(counts=None), 1), (dict(stats=None), 1),
     (dict(psum=ODD), 9), (dict(ws_bytes=100), 6), (dict(gate=2), 5), (dict(k=0), 3), (dict(h=60), 7),
 ])
@@ -153,10 +153,10 @@ def test_balance_workspace_bytes():
     assert R.balance_workspace_bytes(bf, 262144, 2048, 32, 4096, 8) == route + 2 * 256 * 4096 * 4
     route33 = R.workspace_bytes(False, bf, 33, 2048, 32, 4096, 8, 0, True)
     assert R.balance_workspace_bytes(bf, 33, 2048, 32, 4096, 8) == route33 + 2 * 2 * 4096 * 4
-    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 5888, 8) > 0
-    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 5889, 8) == 0     # routing LDS of the k <= 8 kernel
-    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 14720, 4) > 0
-    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 14721, 4) == 0
+    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 65535, 8) > 0
+    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 65537, 8) == 0    # 16-bit sweep positions
+    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 65535, 4) > 0
+    assert R.balance_workspace_bytes(bf, 10, 2048, 32, 65537, 4) == 0
     assert R.balance_workspace_bytes(R.MORE_DT_F32, 10, 2048, 32, 4096, 8) == 0
     assert R.balance_workspace_bytes(bf, 10, 2048, 128, 4096, 8) == 0
     assert R.balance_workspace_bytes(bf, 10, 4608, 16, 4096, 8) > 0       # R1 resident in LDS

@@ -127,6 +127,8 @@ def test_balance_configs(oracle_lib, cfg, n, gate):
 
 @pytest.mark.parametrize("N,h,r,M,k,bias", [
     (1, 256, 32, 4096, 8, True),       # a single token
+    (300, 256, 32, 6000, 8, True),     # M past the earlier LDS-staged bias limit, ragged last tile
+    (200, 256, 16, 20000, 4, True),    # M past the bias-descending order's limit (index order)
     (33, 512, 16, 1000, 4, True),      # ragged block, ragged expert tiles (padding positions)
     (700, 256, 32, 1000, 8, False),    # no bias: plain two passes
     (64, 128, 16, 8, 8, True),         # k = M: every expert selected by every token

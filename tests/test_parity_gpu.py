@@ -262,10 +262,17 @@ PATH_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["split", "slice", "pc", "lock", "stream", "none"])
+@pytest.fixture
+def route_paths():
+    """Restrict the kernel forms for one test; every form is allowed again after it."""
+    yield R.set_route_paths
+    R.set_route_paths(None)
+
+
+@pytest.mark.parametrize("path", ["split", "pc", "lock", "stream", "none"])
 @pytest.mark.parametrize("cfg,n,gate", PATH_CASES, ids=[f"{c.name}-{n}-g{g}" for c, n, g in PATH_CASES])
-def test_kernel_paths(oracle_lib, monkeypatch, path, cfg, n, gate):
-    monkeypatch.setenv("MORE_ROUTE_PATHS", path)
+def test_kernel_paths(oracle_lib, route_paths, path, cfg, n, gate):
+    route_paths(path)
     X = cfg.x_rows(0, 0, n, n_total=cfg.N)
     R1, R2, b = cfg.weights(0)
     check_lowrank(oracle_lib, X, R1, R2, b, cfg.k, gate, f"{cfg.name}-path-{path}")
