@@ -293,7 +293,7 @@ size_t more_route_workspace_bytes(int fullrank, more_dtype dt, int64_t N, int64_
 
 /*
  * Testing aid: restrict the kernel forms the low-rank routing calls may take
- * to a comma-separated subset of "split,pc,lock,stream" (the plain kernel,
+ * to a comma-separated subset of "split,ring,pc,lock,stream" (the plain kernel,
  * which fits every shape, always remains; an empty subset such as "none"
  * leaves only it).  NULL or "" allows every form again.  Every form computes
  * the same selection and gates; this only lets tests check each of them on

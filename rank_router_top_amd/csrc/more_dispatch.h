@@ -81,7 +81,7 @@ size_t proj_lds_bytes(int r16, int ksp);
 // Expert sweep with the up-projection tiles shared through LDS (the routing
 // half of the two-kernel form): bf16, k <= 8, r <= 64, M <= 65536.
 typedef void (*sweep_fn)(SweepArgs);
-constexpr int kSwCons = 8;   // consumer waves (+1 loader), one workgroup per CU
+constexpr int kSwCons = 8;   // consumer waves (+ kSwLoaders loaders), one workgroup per CU
 sweep_fn pick_sweep(bool full, bool lse, int kmax, int r16);
 size_t sweep_lds_bytes(int kmax, int r16);
 

@@ -148,17 +148,17 @@ more_status validate(int fullrank, more_dtype dt, const void* X, int64_t N, int6
 // Kernel paths of the low-rank router, in the order they are tried (measured
 // fastest first on the workloads they share).  Each call takes the first one
 // whose shape envelope fits.  A testing aid can restrict the candidates to a
-// subset of "split,pc,lock,stream" (the plain kernel always remains, so that
+// subset of "split,ring,pc,lock,stream" (the plain kernel always remains, so that
 // every path can be checked on the shapes a faster one would take): the
 // environment variable MORE_ROUTE_PATHS, read once at the first routing call,
 // or more_set_route_paths() at any time.
-enum { kPathPc = 1, kPathLock = 4, kPathStream = 8, kPathSplit = 16, kPathAll = 31 };
+enum { kPathPc = 1, kPathLock = 4, kPathStream = 8, kPathSplit = 16, kPathRing = 32, kPathAll = 63 };
 
 int parse_paths(const char* names) {
   if (!names || !*names) return kPathAll;
   int mask = 0;
   static const struct { const char* name; int bit; } table[] = {
-      {"split", kPathSplit}, {"pc", kPathPc}, {"lock", kPathLock}, {"stream", kPathStream}};
+      {"split", kPathSplit}, {"ring", kPathRing}, {"pc", kPathPc}, {"lock", kPathLock}, {"stream", kPathStream}};
   for (const char* p = names; *p;) {
     const char* e = strchr(p, ',');
     const size_t n = e ? (size_t)(e - p) : strlen(p);
@@ -183,32 +183,32 @@ bool path_allowed(int path) {
   return (m & path) != 0;
 }
 
-// Whether the two-kernel path has an instance for this shape (LDS included).
-bool split_fits(int kmax, const Layout& L, int64_t h) {
+// Whether the two-kernel path has an instance for this shape (LDS included),
+// with the routing kernel reading the R2 tiles itself (ring = false) or
+// through the workgroup's LDS ring (ring = true).
+bool split_fits(int kmax, const Layout& L, int64_t h, bool ring) {
   if (!split_shape_ok(kmax, L.r16, L.Mpad)) return false;
   int ksp = 0;
   bool tail = false;
   proj_ksteps(h, L.r16, &ksp, &tail);
-  return (long long)proj_lds_bytes(L.r16, ksp) <= kLdsBytes && (long long)sweep_lds_bytes(kmax, L.r16) <= kLdsBytes;
+  const long long rt = ring ? (long long)sweep_lds_bytes(kmax, L.r16) : (long long)route_lds_bytes(kmax, L.Mpad);
+  return (long long)proj_lds_bytes(L.r16, ksp) <= kLdsBytes && rt <= kLdsBytes;
 }
 
 // Two kernels: projection (R1 resident in LDS) writes z of every 32-token
 // block to the token scratch behind the packed weights, routing sweeps it.
 // lse_mode: pass 1 covers every tile and lse is written (implied by full).
 more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int kmax, bool full, bool lse_mode,
-                         char* ws, hipStream_t stream) {
+                         bool ring, char* ws, hipStream_t stream) {
   int ksp = 0;
   bool tail = false;
   proj_ksteps(h, L.r16, &ksp, &tail);
   const size_t pj_lds = proj_lds_bytes(L.r16, ksp);
-  const size_t sw_lds = sweep_lds_bytes(kmax, L.r16);
   proj_fn pf = pick_proj(L.r16, tail);
-  sweep_fn sf = pick_sweep(full, lse_mode, kmax, L.r16);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipFuncSetAttribute((const void*)pf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pj_lds) != hipSuccess ||
-      hipFuncSetAttribute((const void*)sf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sw_lds) != hipSuccess)
+      hipFuncSetAttribute((const void*)pf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pj_lds) != hipSuccess)
     return MORE_ERR_HIP;
   const int64_t nb = (a.N + kTile - 1) / kTile;
   if (nb > (int64_t)1 << 30) return MORE_ERR_BAD_SHAPE;
@@ -226,6 +226,26 @@ more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int k
   const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kProjWaves - 1) / kProjWaves));
   hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, stream, pa);
   if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
+  if (!ring) {
+    // every wave reads the R2 tiles from memory itself
+    const size_t rt_lds = route_lds_bytes(kmax, L.Mpad);
+    route_fn rf = pick_route(full, lse_mode, kmax, L.r16);
+    if (hipFuncSetAttribute((const void*)rf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rt_lds) != hipSuccess)
+      return MORE_ERR_HIP;
+    RouteArgs ra;
+    ra.base = a;
+    ra.base.out_lse = lse_mode ? a.out_lse : nullptr;
+    ra.Z = pa.Z;
+    ra.NB = (int)nb;
+    ra.pre = std::min(L.NT, kPcSeedTiles);
+    const int64_t rg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kRouteWaves - 1) / kRouteWaves));
+    hipLaunchKernelGGL(rf, dim3((unsigned)rg), dim3(64 * kRouteWaves), rt_lds, stream, ra);
+    return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+  }
+  const size_t sw_lds = sweep_lds_bytes(kmax, L.r16);
+  sweep_fn sf = pick_sweep(full, lse_mode, kmax, L.r16);
+  if (hipFuncSetAttribute((const void*)sf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sw_lds) != hipSuccess)
+    return MORE_ERR_HIP;
   SweepArgs sa;
   sa.Z = pa.Z;
   sa.R2p = a.R2p;
@@ -246,12 +266,13 @@ more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int k
   const int64_t sg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kSwCons - 1) / kSwCons));
   // the loader's sequence (rounds x (seed + sweep) tiles) must fit an int
   if ((nb / (sg * kSwCons) + 1) * 2 * (int64_t)L.NT >= ((int64_t)1 << 30)) return MORE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL(sf, dim3((unsigned)sg), dim3(64 * (kSwCons + 1)), sw_lds, stream, sa);
+  hipLaunchKernelGGL(sf, dim3((unsigned)sg), dim3(64 * (kSwCons + kSwLoaders)), sw_lds, stream, sa);
   return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 
 bool balance_layout(more_dtype dt, const Layout& L, int64_t N, int64_t h, int64_t M, int32_t k, BalLayout* B) {
-  if (dt != MORE_DT_BF16 || L.ksq <= 0 || L.r16 > 4 || k > 8 || !split_fits(kmax_for(k), L, h)) return false;
+  if (dt != MORE_DT_BF16 || L.ksq <= 0 || L.r16 > 4 || k > 8) return false;
+  if (!split_fits(kmax_for(k), L, h, false) && !split_fits(kmax_for(k), L, h, true)) return false;
   const int64_t nb = N > 0 ? (N + kTile - 1) / kTile : 0;
   B->slots = (int)std::min<int64_t>(kBalSlots, std::max<int64_t>(nb, 1));
   B->off_z = L.total;
@@ -436,8 +457,12 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   a.out_lse = full ? lse : nullptr;
   const size_t shmem = (size_t)waves * log_bytes(kmax);
   const size_t zbytes = z_scratch_bytes(dt, L, N);
-  if (zbytes > 0 && workspace_bytes >= L.total + zbytes && split_fits(kmax, L, h) && path_allowed(kPathSplit))
-    return launch_split(a, L, h, kmax, full, full, ws, (hipStream_t)stream);
+  if (zbytes > 0 && workspace_bytes >= L.total + zbytes) {
+    if (path_allowed(kPathSplit) && split_fits(kmax, L, h, false))
+      return launch_split(a, L, h, kmax, full, full, false, ws, (hipStream_t)stream);
+    if (path_allowed(kPathRing) && split_fits(kmax, L, h, true))
+      return launch_split(a, L, h, kmax, full, full, true, ws, (hipStream_t)stream);
+  }
   const size_t pc_lds = (dt == MORE_DT_BF16 && L.ksq > 0) ? pc_lds_bytes(kmax, L.r16, L.Mpad) : 0;
   if (pc_lds > 0 && (long long)pc_lds <= kLdsBytes && path_allowed(kPathPc)) {
     // Producer/consumer kernel: one 12-wave workgroup per CU, persistent.
@@ -576,7 +601,7 @@ more_status more_lowrank_balance_packed(more_dtype dt, const void* X, int64_t N,
   a.out_logit = topk_logit;
   a.out_lse = lse;
   // 1. forward: z to the scratch, top-k + gates + lse (pass 1 over every tile)
-  st = launch_split(a, L, h, kmax_for(k), full, true, ws, hs);
+  st = launch_split(a, L, h, kmax_for(k), full, true, !split_fits(kmax_for(k), L, h, false), ws, hs);
   if (st != MORE_OK) return st;
   // 2. second sweep: psum; counts; column sums; L_bal and H_norm
   const int64_t nb = (N + kTile - 1) / kTile;

@@ -76,14 +76,18 @@ struct SweepArgs {
   int spin_limit;            // polls before a wait gives up
 };
 
-// LDS map.  Flag words (ints): published (tiles of the sequence in the ring
-// so far; tile g sits in slot g % RING), prog[NC] (tiles each consumer has
-// finished reading), abort.
+// Loader waves per workgroup: loader i copies the sequence tiles g = i (mod
+// kSwLoaders), so that the copies of several tiles are issued at once.
+constexpr int kSwLoaders = 2;
+
+// LDS map.  Flag words (ints): published[kSwLoaders] (loader i has copied its
+// tiles below published[i]; tile g sits in slot g % RING), prog[NC] (tiles
+// each consumer has finished reading), abort.
 template <int R16, int NC, int RING, int CAP, int KMAX>
 struct SwLds {
   static constexpr int TB = R16 * 1024 + 256;   // ring slot: R16 A operands + 64 bias words
-  static constexpr int kPub = 0, kProg = 1, kAbort = 1 + NC;
-  static_assert(NC + 2 <= 64, "flag words");
+  static constexpr int kPub = 0, kProg = kSwLoaders, kAbort = kSwLoaders + NC;
+  static_assert(NC + kSwLoaders + 1 <= 64, "flag words");
   static constexpr int kRing = 256;
   static constexpr int kCons = kRing + RING * TB;
   static constexpr int kLogV = 0;                        // [CAP][64] 4 logits (16 B)
@@ -197,34 +201,68 @@ __device__ __noinline__ float2 sw_tighten(float thr, int cnt, SwLog lg, int lane
   return make_float2(t2, __int_as_float(w));
 }
 
-// Main-sweep logging of one tile (acc: this lane's 16 exact logits, bias
-// included, -inf on padding rows; pos_base = 32 t + 4 hf; register 4q + e is
-// sweep row 8q + 4hf + e).  Appends are branch-free inside a group that has a
-// candidate in some lane: every lane writes slot cnt, only a hit advances it.
+// Per-group appends with a capacity check before each (out of line: taken
+// when a lane's log is nearly full even after a tightening, i.e. with many
+// exact ties).  Whole wave active; returns (thr, count as int bits).
 template <int KMAX, int CAP>
-__device__ __forceinline__ void sw_log_tile(TwoPassState<KMAX>& st, const floatx16& acc, int pos_base, SwLog lg,
-                                            int lane, bool hi_half, int k, const int* __restrict__ perm) {
-  floatx4 g;
+__device__ __noinline__ float2 sw_log_slow(floatx16 acc, float thr, int cnt, int pos_base, SwLog lg, int lane,
+                                           bool hi_half, int k, const int* __restrict__ perm) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    g[q] = fmaxf(fmaxf(acc[4 * q], acc[4 * q + 1]), fmaxf(acc[4 * q + 2], acc[4 * q + 3]));
-  const float tmax = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
-  if (any_lane(tmax >= st.thr)) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (any_lane(g[q] >= st.thr)) {
-        if (any_lane(st.cnt >= CAP)) {
-          const float2 r = sw_tighten<KMAX, CAP>(st.thr, st.cnt, lg, lane, hi_half, k, perm);
-          st.thr = r.x;
-          st.cnt = __float_as_int(r.y);
-        }
-        lg.val[st.cnt * kWave + lane] = floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-        lg.pos[st.cnt * kWave + lane] = (uint16_t)(pos_base + 8 * q);
-        st.cnt += (g[q] >= st.thr) ? 1 : 0;
+  for (int q = 0; q < 4; ++q) {
+    const float g = fmaxf(fmaxf(acc[4 * q], acc[4 * q + 1]), fmaxf(acc[4 * q + 2], acc[4 * q + 3]));
+    if (any_lane(g >= thr)) {
+      if (any_lane(cnt >= CAP)) {
+        const float2 r = sw_tighten<KMAX, CAP>(thr, cnt, lg, lane, hi_half, k, perm);
+        thr = r.x;
+        cnt = __float_as_int(r.y);
+      }
+      if (g >= thr) {
+        lg.val[cnt * kWave + lane] = floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        lg.pos[cnt * kWave + lane] = (uint16_t)(pos_base + 8 * q);
+        ++cnt;
       }
     }
-    // the appends complete here, so later LDS waits need not count them
-    lds_drain();
+  }
+  return make_float2(thr, __int_as_float(cnt));
+}
+
+// Main-sweep logging of one tile (acc: this lane's 16 exact logits, bias
+// included, -inf on padding rows; gq: the maxima of its four 4-logit groups;
+// pos_base = 32 t + 4 hf; register 4q + e is sweep row 8q + 4hf + e).  A lane
+// appends each of its groups whose maximum reaches thr (16 bytes + the 16-bit
+// sweep position of the group's first logit).
+template <int KMAX, int CAP>
+__device__ __forceinline__ void sw_log_tile(TwoPassState<KMAX>& st, const floatx16& acc, const floatx4& gq,
+                                            int pos_base, SwLog lg, int lane, bool hi_half, int k,
+                                            const int* __restrict__ perm) {
+  const float tmax = fmaxf(fmaxf(gq[0], gq[1]), fmaxf(gq[2], gq[3]));
+  if (!any_lane(tmax >= st.thr)) return;
+  auto hits = [&]() {
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) n += gq[q] >= st.thr ? 1 : 0;
+    return n;
+  };
+  // The appends below write slot cnt in every lane (a lane without a hit
+  // writes its next free slot, which stays free), so cnt + hits must stay
+  // below CAP: the last slot is the spare of a full lane.
+  if (any_lane(st.cnt > CAP - 5) && any_lane(st.cnt + hits() > CAP - 1)) {
+    // some lane's appends would not fit: tighten first
+    const float2 r = sw_tighten<KMAX, CAP>(st.thr, st.cnt, lg, lane, hi_half, k, perm);
+    st.thr = r.x;
+    st.cnt = __float_as_int(r.y);
+    if (any_lane(st.cnt + hits() > CAP - 1)) {
+      const float2 r2 = sw_log_slow<KMAX, CAP>(acc, st.thr, st.cnt, pos_base, lg, lane, hi_half, k, perm);
+      st.thr = r2.x;
+      st.cnt = __float_as_int(r2.y);
+      return;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    lg.val[st.cnt * kWave + lane] = floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    lg.pos[st.cnt * kWave + lane] = (uint16_t)(pos_base + 8 * q);
+    st.cnt += gq[q] >= st.thr ? 1 : 0;
   }
 }
 
@@ -395,7 +433,7 @@ __device__ __forceinline__ bool sw_wait_ge(flag_ptr f, int need, flag_ptr abort_
 }
 
 template <int KMAX, int R16, bool LSE, bool FULL, int NC, int RING, int CAP>
-__global__ __launch_bounds__(64 * (NC + 1)) void sweep_kernel(SweepArgs a) {
+__global__ __launch_bounds__(64 * (NC + kSwLoaders)) void sweep_kernel(SweepArgs a) {
   typedef SwLds<R16, NC, RING, CAP, KMAX> L;
   typedef TpStage<KMAX> S;
   extern __shared__ __align__(16) char sw_lds[];
@@ -403,7 +441,8 @@ __global__ __launch_bounds__(64 * (NC + 1)) void sweep_kernel(SweepArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x, w = blockIdx.x;
   const int NT = a.NT;
-  const int P = min(max(__builtin_amdgcn_readfirstlane(__float_as_int(a.wstat[2])), 1), NT);
+  // seed tiles, even (NT is even: the expert count is padded to a multiple of 64)
+  const int P = min((max(__builtin_amdgcn_readfirstlane(__float_as_int(a.wstat[2])), 1) + 1) & ~1, NT);
   const int Lseq = P + NT;
   if (threadIdx.x < 64) ((int*)sw_lds)[threadIdx.x] = 0;
   __syncthreads();
@@ -413,16 +452,21 @@ __global__ __launch_bounds__(64 * (NC + 1)) void sweep_kernel(SweepArgs a) {
   const long long per_round = (long long)G * NC;
   const int rounds = a.NB > (long long)w * NC ? (int)((a.NB - (long long)w * NC + per_round - 1) / per_round) : 0;
 
-  if (wave == NC) {
-    // ---------------------------------------------------------------- loader
-    constexpr int LEAD = 4;          // tiles whose copies may still be in flight
+  if (wave >= NC) {
+    // ---------------------------------------------------------------- loaders
+    // own tiles whose copies may still be in flight; the ring must hold them
+    // plus the two tiles a consumer reads ahead (no circular wait)
+    constexpr int LEAD = RING / kSwLoaders - 2 < 4 ? RING / kSwLoaders - 2 : 4;
     constexpr int DPT = R16 + 1;     // copies per tile
+    static_assert(LEAD >= 1 && RING >= kSwLoaders * (LEAD + 1) + 1, "ring depth");
+    const int li = wave - NC;
     const int total = rounds * Lseq;
     const rsrc_t r2d = make_rsrc(a.R2p, NT * R16 * 1024);
     const rsrc_t bqd = make_rsrc(a.biasq, NT * 256);
-    int jseq = 0, slot_i = 0;   // g % Lseq and g % RING, kept incrementally
-    int freed = 0;              // every consumer has read the tiles below this one
-    for (int g = 0; g < total; ++g) {
+    int jseq = li, slot_i = li;   // g % Lseq and g % RING, kept incrementally
+    int freed = 0;                // every consumer has read the tiles below this one
+    int n = 0;                    // own tiles issued
+    for (int g = li; g < total; g += kSwLoaders, ++n) {
       if (g - RING >= freed) {
         // slot g % RING is free once every consumer has read tile g - RING
         for (int it = 0;; ++it) {
@@ -447,18 +491,20 @@ __global__ __launch_bounds__(64 * (NC + 1)) void sweep_kernel(SweepArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r2d, (lds_void*)(slot + m * 1024), 16, lane * 16,
                                                  (t * R16 + m) * 1024, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(bqd, (lds_void*)(slot + R16 * 1024), 4, lane * 4, t * 256, 0, 0);
-      if (g >= LEAD) {
-        // the copies of tile g - LEAD (and older) have landed
+      if (n >= LEAD) {
+        // the copies of own tile g - LEAD * kSwLoaders (and older) have landed
         wait_vmcnt<LEAD * DPT>();
         asm volatile("" ::: "memory");
-        *published = g - LEAD + 1;
+        published[li] = g - LEAD * kSwLoaders + 1;
       }
-      if (++jseq == Lseq) jseq = 0;
-      if (++slot_i == RING) slot_i = 0;
+      jseq += kSwLoaders;
+      if (jseq >= Lseq) jseq -= Lseq;
+      slot_i += kSwLoaders;
+      if (slot_i >= RING) slot_i -= RING;
     }
     wait_vmcnt<0>();
     asm volatile("" ::: "memory");
-    *published = total;
+    published[li] = total;
     return;
   }
 
@@ -469,10 +515,6 @@ __global__ __launch_bounds__(64 * (NC + 1)) void sweep_kernel(SweepArgs a) {
   char* cl = sw_lds + L::kCons + c * L::kConsBytes;
   const SwLog lg{(lds_f4*)(cl + L::kLogV), (lds_u16*)(cl + L::kLogP)};
   lds_f32* stg = (lds_f32*)(cl + L::kStage);
-  const float r2max = a.wstat[0], babs = a.wstat[1];
-  // the seed tiles' smallest biases: lane t holds tile t's (read with v_readlane;
-  // a per-tile vector load would wait on the whole vector-memory counter)
-  const float bmv = lane < NT ? a.bmin[lane] : -__builtin_inff();
   // the ones operand of the bias MFMA: K slots 0 and 1 of every token column
   bf16x8 ones;
 #pragma unroll
@@ -489,11 +531,53 @@ __global__ __launch_bounds__(64 * (NC + 1)) void sweep_kernel(SweepArgs a) {
       l[m] = buf_load(zd, lane * 16 + (R16 + m) * 1024, 0);
     }
   };
+  const int total = rounds * Lseq;   // the loader's sequence
+  int pub = 0;                       // tiles known to be published
+  bool stalled = false;              // a bounded wait gave up (results are void)
+  // sequence tile g's operands -> (op, bq).  Reads past the sequence end
+  // re-read its last tile (the prefetch of a round that does not follow).
+  auto fetch = [&](int g, bf16x8 (&op)[R16], uint32_t& bq) {
+    g = min(g, total - 1);
+    if (g >= pub) {
+      // every tile below the smallest published count is in the ring
+      for (int it = 0;; ++it) {
+        int mn = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < kSwLoaders; ++i) mn = min(mn, __builtin_amdgcn_readfirstlane(published[i]));
+        pub = mn;
+        if (g < pub) break;
+        if (__builtin_amdgcn_readfirstlane(*abort_word) != 0 || it >= a.spin_limit) {
+          *abort_word = 1;
+          stalled = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      asm volatile("" ::: "memory");
+    }
+    lds_cchar* slot = (lds_cchar*)(sw_lds + L::kRing + ((unsigned)g % RING) * L::TB);
+#pragma unroll
+    for (int m = 0; m < R16; ++m) op[m] = *(lds_cbf16x8*)(slot + m * 1024 + lane * 16);
+    bq = *(lds_cu32*)(slot + R16 * 1024 + lane * 4);
+  };
+  // tile g has been read once its MFMAs are issued: the asm makes the operand
+  // registers (hence the LDS reads) complete before the progress word moves
+  auto consumed = [&](int g, const bf16x8 (&op)[R16], uint32_t bq) {
+#pragma unroll
+    for (int m = 0; m < R16; ++m) asm volatile("" ::"v"(op[m]));
+    asm volatile("" ::"v"(bq) : "memory");
+    prog[c] = g + 1;
+  };
+
   bf16x8 zh[R16], zl[R16], nh[R16], nl[R16];
-  if (rounds > 0) zload((long long)w * NC + c, nh, nl);
-  bool ok = true;
-  int pub = 0;   // tiles known to be published
-  for (int round = 0; round < rounds && ok; ++round) {
+  bf16x8 opA[R16], opB[R16];
+  uint32_t bqA = 0, bqB = 0;
+  if (rounds > 0) {
+    zload((long long)w * NC + c, nh, nl);
+    fetch(0, opA, bqA);
+    fetch(1, opB, bqB);
+  }
+  for (int round = 0; round < rounds && !stalled; ++round) {
     const long long b = ((long long)round * G + w) * NC + c;
     if (b >= a.NB) break;
 #pragma unroll
@@ -502,125 +586,104 @@ __global__ __launch_bounds__(64 * (NC + 1)) void sweep_kernel(SweepArgs a) {
       zl[m] = nl[m];
     }
     if (b + per_round < a.NB) zload(b + per_round, nh, nl);
-    // eps of the token (both lanes hold half of z each)
-    float sl = 0.f, sh = 0.f;
+    // exact logits of one tile: the bias (hi + lo against the ones operand),
+    // then z_hi and z_lo against the tile's R2 operands
+    auto mfmas = [&](const bf16x8 (&op)[R16], uint32_t bq) -> floatx16 {
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{bq, 0u, 0u, 0u});
+      floatx16 acc = mfma_bf16(bop, ones, zero);
 #pragma unroll
-    for (int m = 0; m < R16; ++m)
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(op[m], zh[m], acc);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float u = (float)zl[m][e], v = (float)zh[m][e];
-        sl = __builtin_fmaf(u, u, sl);
-        sh = __builtin_fmaf(v, v, sh);
-      }
-    sl += partner_f32(sl, hi);
-    sh += partner_f32(sh, hi);
-    const float eps = __builtin_sqrtf(sl) * r2max + 0x1p-15f * (__builtin_sqrtf(sh) * r2max + babs);
-
+      for (int m = 0; m < R16; ++m) acc = mfma_bf16(op[m], zl[m], acc);
+      return acc;
+    };
     TwoPassState<KMAX> st;
     st.init(a.k);
     const int g0 = round * Lseq;
-    // two operand buffers and two accumulators, used alternately (the buffer
-    // index is a compile-time constant in each half of the loop body)
-    bf16x8 opA[R16], opB[R16];
-    uint32_t bqA = 0, bqB = 0;
+    // seed: the lane's tile maximum is the exact logit of one expert; the k
+    // largest of these over both lanes bound the token's k-th logit from below
+    auto seed = [&](const floatx16& acc) { med3_insert<KMAX>(st.L, max16(acc)); };
+    // main-sweep tile, straight-line part: group maxima and the running normaliser
+    auto pre = [&](const floatx16& acc) -> floatx4 {
+      floatx4 gq;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        gq[q] = fmaxf(fmaxf(acc[4 * q], acc[4 * q + 1]), fmaxf(acc[4 * q + 2], acc[4 * q + 3]));
+      if (LSE) tp_lse_tile<KMAX>(st, acc, gq);
+      return gq;
+    };
+    // main-sweep tile t, branching part: the appends, and the scheduled tightening
+    auto post = [&](const floatx16& acc, const floatx4& gq, int t) {
+      sw_log_tile<KMAX, CAP>(st, acc, gq, kTile * t + 4 * hf, lg, lane, hi, a.k, a.perm);
+      if (t == kTightenTile - 1 && NT > kTightenTile) {
+        const float2 r = sw_tighten<KMAX, CAP>(st.thr, st.cnt, lg, lane, hi, a.k, a.perm);
+        st.thr = r.x;
+        st.cnt = __float_as_int(r.y);
+      }
+    };
+    // Interleave the MFMAs of one tile with the straight-line VALU work of the
+    // previous one in the instruction stream (the wave issues VALU work while
+    // its MFMAs occupy the matrix pipe).
+    auto interleave = [&]() {
+#pragma unroll
+      for (int i = 0; i < 2 * R16 + 1; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    };
+    // keep a value's computation in front of this point (the compiler would
+    // otherwise sink it past the polls, away from the MFMAs it should overlap)
+    auto pin_seed = [&]() {
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) asm volatile("" ::"v"(st.L[i]));
+    };
+    auto pin4 = [&](const floatx4& v) { asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])); };
+    // Software pipeline: the MFMAs of the next tile are issued with the VALU
+    // work of the current one.  Entering: opA / opB hold sequence tiles g0 and
+    // g0 + 1 (P and Lseq are even).
     floatx16 accA, accB;
-    // tile j's operands -> (op, bq), once the loader has published it (the
-    // published count is polled only when the cached one runs out)
-    auto fetch = [&](int j, bf16x8 (&op)[R16], uint32_t& bq) -> bool {
-      const int g = g0 + j;
-      if (g >= pub) {
-        if (!sw_wait_ge(published, g + 1, abort_word, a.spin_limit)) return false;
-        pub = __builtin_amdgcn_readfirstlane(*published);
-        asm volatile("" ::: "memory");
-      }
-      lds_cchar* slot = (lds_cchar*)(sw_lds + L::kRing + (g % RING) * L::TB);
-#pragma unroll
-      for (int m = 0; m < R16; ++m) op[m] = *(lds_cbf16x8*)(slot + m * 1024 + lane * 16);
-      bq = *(lds_cu32*)(slot + R16 * 1024 + lane * 4);
-      return true;
-    };
-    // the MFMAs of tile j
-    auto mfmas = [&](int j, const bf16x8 (&op)[R16], uint32_t bq) -> floatx16 {
-      floatx16 acc;
-      if (j < P) {
-        acc = mfma_bf16(op[0], zh[0], zero);
-#pragma unroll
-        for (int m = 1; m < R16; ++m) acc = mfma_bf16(op[m], zh[m], acc);
-      } else {
-        const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{bq, 0u, 0u, 0u});
-        acc = mfma_bf16(bop, ones, zero);
-#pragma unroll
-        for (int m = 0; m < R16; ++m) acc = mfma_bf16(op[m], zh[m], acc);
-#pragma unroll
-        for (int m = 0; m < R16; ++m) acc = mfma_bf16(op[m], zl[m], acc);
-      }
-      return acc;
-    };
-    // the VALU side of tile j (its accumulator holds the logits)
-    auto valu = [&](int j, const floatx16& acc_j) {
-      if (j < P) {
-        // seed: the tile maximum plus the tile's smallest bias is at most
-        // (up to eps) the logit of one real expert
-        const float bm = j < kWave ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bmv), j)) : a.bmin[j];
-        const float lb = max16(acc_j) + bm;
-        med3_insert<KMAX>(st.L, lb);
-      } else {
-        const int t = j - P;
-        if (LSE) {
-          floatx4 gq;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            gq[q] = fmaxf(fmaxf(acc_j[4 * q], acc_j[4 * q + 1]), fmaxf(acc_j[4 * q + 2], acc_j[4 * q + 3]));
-          tp_lse_tile<KMAX>(st, acc_j, gq);
-        }
-        sw_log_tile<KMAX, CAP>(st, acc_j, kTile * t + 4 * hf, lg, lane, hi, a.k, a.perm);
-        if (t == kTightenTile - 1 && NT > kTightenTile) {
-          const float2 r = sw_tighten<KMAX, CAP>(st.thr, st.cnt, lg, lane, hi, a.k, a.perm);
-          st.thr = r.x;
-          st.cnt = __float_as_int(r.y);
-        }
-      }
-      if (j == P - 1) {
-        // end of the seed: the token's threshold
-        tp_threshold<KMAX>(st, hi, a.k);
-        st.thr -= eps;
-      }
-    };
-    // tile j has been read once its MFMAs are issued: the asm makes its operand
-    // registers (hence the LDS reads) complete before the progress word moves
-    auto consumed = [&](int j, const bf16x8 (&op)[R16], uint32_t bq) {
-#pragma unroll
-      for (int m = 0; m < R16; ++m) asm volatile("" ::"v"(op[m]));
-      asm volatile("" ::"v"(bq) : "memory");
-      prog[c] = g0 + j + 1;
-    };
-    // software pipeline: the MFMAs of tile j run while the VALU works on tile j - 1
-    ok = fetch(0, opA, bqA);
-    int j = 0;
-    for (; j + 1 < Lseq && ok; j += 2) {
-      ok = fetch(j + 1, opB, bqB);
-      if (!ok) break;
-      accA = mfmas(j, opA, bqA);
-      consumed(j, opA, bqA);
-      if (j >= 1) valu(j - 1, accB);
+    accA = mfmas(opA, bqA);
+    consumed(g0, opA, bqA);
+    fetch(g0 + 2, opA, bqA);
+    for (int j = 0; j < P; j += 2) {
+      accB = mfmas(opB, bqB);
+      seed(accA);
+      interleave();
+      pin_seed();
+      consumed(g0 + j + 1, opB, bqB);
+      fetch(g0 + j + 3, opB, bqB);
+      accA = mfmas(opA, bqA);
+      seed(accB);
+      interleave();
+      pin_seed();
+      consumed(g0 + j + 2, opA, bqA);
+      fetch(g0 + j + 4, opA, bqA);
+    }
+    tp_threshold<KMAX>(st, hi, a.k);
+    // accA: sequence tile g0 + P (main tile 0) in flight
+    for (int j = P; j < Lseq; j += 2) {
+      accB = mfmas(opB, bqB);
+      const floatx4 gA = pre(accA);
+      interleave();
+      pin4(gA);
+      consumed(g0 + j + 1, opB, bqB);
+      fetch(g0 + j + 3, opB, bqB);
+      post(accA, gA, j - P);
+      floatx4 gB;
       if (j + 2 < Lseq) {
-        ok = fetch(j + 2, opA, bqA);
-        if (!ok) break;
+        accA = mfmas(opA, bqA);
+        gB = pre(accB);
+        interleave();
+        pin4(gB);
+        consumed(g0 + j + 2, opA, bqA);
+        fetch(g0 + j + 4, opA, bqA);
+      } else {
+        gB = pre(accB);
       }
-      accB = mfmas(j + 1, opB, bqB);
-      consumed(j + 1, opB, bqB);
-      valu(j, accA);
+      post(accB, gB, j + 1 - P);
     }
-    if (!ok) break;
-    // tail: Lseq odd leaves tile Lseq - 1 (its operands are in opA)
-    if (j < Lseq) {
-      accA = mfmas(j, opA, bqA);
-      consumed(j, opA, bqA);
-      if (j >= 1) valu(j - 1, accB);
-      valu(j, accA);
-    } else {
-      valu(Lseq - 1, accB);
-    }
+    // opA / opB now hold the next round's first two tiles
+    if (stalled) break;
 
     // finish: results (sweep positions in the idx words) into the result block
     sw_finish<KMAX, FULL, LSE>(st, lg, lane, hi, a.perm, a.k, a.out_logit != nullptr, stg);
@@ -671,7 +734,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void sweep_kernel(SweepArgs a) {
     // the result block is rewritten by the next finish only after these reads
     lds_drain();
   }
-  if (!ok) sw_fail(a.status, 1);
+  if (stalled) sw_fail(a.status, 1);
   // retire: the loader no longer waits for this consumer
   asm volatile("" ::: "memory");
   prog[c] = 0x7fffffff;

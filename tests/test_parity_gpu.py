@@ -269,7 +269,7 @@ def route_paths():
     R.set_route_paths(None)
 
 
-@pytest.mark.parametrize("path", ["split", "pc", "lock", "stream", "none"])
+@pytest.mark.parametrize("path", ["split", "ring", "pc", "lock", "stream", "none"])
 @pytest.mark.parametrize("cfg,n,gate", PATH_CASES, ids=[f"{c.name}-{n}-g{g}" for c, n, g in PATH_CASES])
 def test_kernel_paths(oracle_lib, route_paths, path, cfg, n, gate):
     route_paths(path)

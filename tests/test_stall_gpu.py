@@ -37,7 +37,15 @@ def spin_limit():
     R.set_spin_limit(0)
 
 
-def test_tiny_spin_limit_reports_stall(oracle_lib, spin_limit):
+@pytest.fixture
+def route_paths():
+    yield R.set_route_paths
+    R.set_route_paths(None)
+
+
+@pytest.mark.parametrize("path", ["split", "ring", "pc"])
+def test_tiny_spin_limit_reports_stall(oracle_lib, spin_limit, route_paths, path):
+    route_paths(path)
     cfg = CF.HEADLINE
     n = 32 * 1024 + 7
     Xn = cfg.x_rows(0, 0, n, n_total=cfg.N)
@@ -48,7 +56,7 @@ def test_tiny_spin_limit_reports_stall(oracle_lib, spin_limit):
     ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     R.pack_lowrank(*d, ws)
     assert R.route_status(ws) == R.MORE_OK
-    say(f"tiny spin limit: N={n}")
+    say(f"tiny spin limit: path {path}, N={n}")
     spin_limit(1)
     R.route_lowrank_packed(X, cfg.r, cfg.M, cfg.k, 0, ws)
     assert R.route_status(ws) == R.MORE_ERR_STALLED
