@@ -60,8 +60,9 @@ typedef void (*proj_fn)(ProjArgs);
 typedef void (*route_fn)(RouteArgs);
 constexpr int kProjWaves = 4;    // projection: one streaming wave per SIMD (+1 writer), one workgroup per CU
 constexpr int kRouteWaves = 8;   // routing: eight waves, one workgroup per CU
-// Projection ring depth (K-steps in flight per wave).
-constexpr int proj_depth(int r16) { return 8; }
+// Projection ring depth (X loads in flight per wave): 16, or 8 at r = 64,
+// where the packed down-projection takes more of the LDS.
+constexpr int proj_depth(int r16) { return r16 >= 4 ? 8 : 16; }
 // K-steps the projection processes (a multiple of its ring depth) and whether
 // the X loads need per-lane column checks.
 inline void proj_ksteps(long long h, int r16, int* ksp, bool* tail) {

@@ -223,7 +223,7 @@ more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int k
   pa.Z = ws + L.total;
   pa.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   pa.status = (int*)(ws + L.off_status);
-  const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kProjWaves - 1) / kProjWaves));
+  const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (2 * nb + kProjWaves - 1) / kProjWaves));
   hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, stream, pa);
   if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
   if (!ring) {
@@ -749,7 +749,7 @@ more_status more_lowrank_backward_packed(more_dtype dt, const void* X, int64_t N
   pa.Z = ws + B.off_z;
   pa.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   pa.status = (int*)(ws + L.off_status);
-  const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (nb + kProjWaves - 1) / kProjWaves));
+  const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (2 * nb + kProjWaves - 1) / kProjWaves));
   hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, hs, pa);
   if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
   // 2. phase 2 (two sweeps) and phase 3

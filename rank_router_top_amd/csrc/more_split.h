@@ -106,8 +106,12 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
   flag_ptr fl = pc_flags(pj_lds);
   flag_ptr full = fl, freed = fl + 8, abort_word = fl + 16;
   const int W = gridDim.x * SW;   // streaming waves in the grid
-  auto nblocks = [&](int s) { const int w = blockIdx.x * SW + s; return (pa.NB - w + W - 1) / W; };
-  auto blk = [&](int s, int jj) -> long long { return (long long)(blockIdx.x * SW + s) + (long long)jj * W; };
+  // Work items are 16-token halves of the 32-token blocks (item i: tokens
+  // 16i .. 16i + 15, block i / 2), handed out grid-stride: at any time the
+  // streaming waves of the grid read adjacent 16-row slabs of X.
+  const int NI = 2 * pa.NB;
+  auto nitems = [&](int s) { const int w = blockIdx.x * SW + s; return (NI - w + W - 1) / W; };
+  auto item = [&](int s, int jj) -> long long { return (long long)(blockIdx.x * SW + s) + (long long)jj * W; };
 
   if (wave == SW) {
     // writer: serve whichever streaming wave has a block ready
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
       bool left = false, did = false;
 #pragma unroll
       for (int s = 0; s < SW; ++s) {
-        if (served[s] >= nblocks(s)) continue;
+        if (served[s] >= nitems(s)) continue;
         left = true;
         if (__builtin_amdgcn_readfirstlane(full[s]) <= served[s]) continue;
         asm volatile("" ::: "memory");   // the slot reads stay after the poll
@@ -128,9 +132,13 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
         for (int q = 0; q < 2 * R16; ++q) v[q] = *(const u32x4*)(slot + q * 1024 + lane * 16);
         lds_drain();
         freed[s] = served[s] + 1;
-        const rsrc_t zd = make_rsrc((char*)pa.Z + (size_t)blk(s, served[s]) * z_block_bytes(R16), z_block_bytes(R16));
+        const long long it = item(s, served[s]);
+        const rsrc_t zd = make_rsrc((char*)pa.Z + (size_t)(it >> 1) * z_block_bytes(R16), z_block_bytes(R16));
+        // the item's 16 tokens are lanes 16g .. 16g + 15 (mod 32) of the block
+        if (((lane >> 4) & 1) == (int)(it & 1)) {
 #pragma unroll
-        for (int q = 0; q < 2 * R16; ++q) __builtin_amdgcn_raw_buffer_store_b128(v[q], zd, q * 1024 + lane * 16, 0, 0);
+          for (int q = 0; q < 2 * R16; ++q) __builtin_amdgcn_raw_buffer_store_b128(v[q], zd, q * 1024 + lane * 16, 0, 0);
+        }
         ++served[s];
         did = true;
       }
@@ -149,33 +157,33 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
     return;
   }
 
-  const int nj = nblocks(wave);
+  const int nj = nitems(wave);
   if (nj <= 0) return;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int rowbytes = pa.h * 2;
-  const int vrow0 = l16 * rowbytes, vrow1 = (16 + l16) * rowbytes;
-  const int vx0 = vrow0 + 16 * q4, vx1 = vrow1 + 16 * q4;
+  const int vrow0 = l16 * rowbytes;
+  const int vx0 = vrow0 + 16 * q4;
   const int NBAT = pa.KSP / D;
-  auto xbase = [&](int jj) -> const char* { return (const char*)pa.X + (size_t)blk(wave, jj) * kTile * rowbytes; };
+  auto xbase = [&](int jj) -> const char* { return (const char*)pa.X + (size_t)item(wave, jj) * 16 * rowbytes; };
   auto xbytes = [&](int jj) -> int {
     if (jj >= nj) return 0;
-    const long long rows = pa.N - blk(wave, jj) * kTile;
-    return (int)((rows < kTile ? rows : kTile) * rowbytes);
+    const long long rows = pa.N - item(wave, jj) * 16;
+    return rows <= 0 ? 0 : (int)((rows < 16 ? rows : 16) * rowbytes);
   };
   lds_cchar* r1l = (lds_cchar*)(pj_lds + L::kR1);
   auto r1op = [&](int s, int rb) -> bf16x8 { return *(lds_cbf16x8*)(r1l + (s * R16 + rb) * 1024 + lane * 16); };
   char* slot = pj_lds + L::kSlots + wave * z_block_bytes(R16);
 
-  bf16x8 xr[D][2];
+  // X ring: D slots of one 16-byte load each (the item's 16 rows x 64 bytes
+  // of K-step s); each load walks on along the same rows, so the two halves
+  // of every 128-byte line are requested back to back.
+  bf16x8 xr[D];
   auto issue = [&](int u, rsrc_t xd, int s) {
     if constexpr (TAIL) {
       const int c2 = 64 * s + 16 * q4;   // byte column of this lane's 8 elements
-      const bool ok = c2 < rowbytes;
-      xr[u][0] = buf_load(xd, ok ? vrow0 + c2 : kOob, 0);
-      xr[u][1] = buf_load(xd, ok ? vrow1 + c2 : kOob, 0);
+      xr[u] = buf_load(xd, c2 < rowbytes ? vrow0 + c2 : kOob, 0);
     } else {
-      xr[u][0] = buf_load(xd, vx0, 64 * s);
-      xr[u][1] = buf_load(xd, vx1, 64 * s);
+      xr[u] = buf_load(xd, vx0, 64 * s);
     }
   };
   const char* cbase = xbase(0);
@@ -191,13 +199,11 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
     }
   }
   for (int jj = 0; jj < nj; ++jj) {
-    floatx4 acc[2][R16];
+    floatx4 acc[R16];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int rb = 0; rb < R16; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < R16; ++rb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[g][rb][v] = 0.f;
+      for (int v = 0; v < 4; ++v) acc[rb][v] = 0.f;
     // down-projection operands: a ring of RP K-steps read from LDS RP-1 steps ahead
     constexpr int RP = 4;
     static_assert(D % RP == 0, "the LDS operand ring must divide the X ring");
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
 #pragma unroll
       for (int rb = 0; rb < R16; ++rb) rr[q][rb] = r1op(q < pa.KSP ? q : pa.KSP - 1, rb);
     for (int sb = 0; sb < NBAT; ++sb) {
-      const bool last = sb == NBAT - 1;   // refill with the next block's first K-steps
+      const bool last = sb == NBAT - 1;   // refill with the next item's first K-steps
       const rsrc_t xd = make_rsrc(last ? nbase : cbase, last ? nbytes : cbytes);
       const int s0 = last ? 0 : (sb + 1) * D;
 #pragma unroll
@@ -217,32 +223,30 @@ __global__ __launch_bounds__(64 * (SW + 1)) void proj_kernel(ProjArgs pa) {
 #pragma unroll
         for (int rb = 0; rb < R16; ++rb) rr[(u + RP - 1) % RP][rb] = r1op(sn, rb);
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int rb = 0; rb < R16; ++rb)
-            acc[g][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rr[u % RP][rb], xr[u][g], acc[g][rb], 0, 0, 0);
+        for (int rb = 0; rb < R16; ++rb)
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rr[u % RP][rb], xr[u], acc[rb], 0, 0, 0);
         issue(u, xd, s0 + u);
-        // slot order: the MFMAs of slot u wait only for slot u's loads
+        // slot order: the MFMAs of slot u wait only for slot u's load
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // acc[g][rb][v] = z[token 16g + l16][rank 16rb + 4q4 + v] -> bf16 hi + lo in
-    // the 32x32x16 B-operand layout: lane 16g + l16 + 32(q4&1), elements
-    // 4(q4>>1) .. +3 of K-step rb; into the slot once the writer has read the
-    // previous block out of it
+    // acc[rb][v] = z[token 16g + l16][rank 16rb + 4q4 + v] (g = item & 1: the
+    // item's half of the block) -> bf16 hi + lo in the 32x32x16 B-operand
+    // layout: lane 16g + l16 + 32(q4&1), elements 4(q4>>1) .. +3 of K-step rb;
+    // into the slot once the writer has read the previous item out of it
     if (!pc_wait(freed + wave, jj, abort_word, pa.spin_limit)) {
       if (pa.status) __hip_atomic_store(pa.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    {
+      const int g = (int)(item(wave, jj) & 1);
       const int off = (16 * g + l16 + 32 * (q4 & 1)) * 16 + 8 * (q4 >> 1);
 #pragma unroll
       for (int rb = 0; rb < R16; ++rb) {
         uint32_t hv[2], lv[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const float f0 = acc[g][rb][2 * h2], f1 = acc[g][rb][2 * h2 + 1];
+          const float f0 = acc[rb][2 * h2], f1 = acc[rb][2 * h2 + 1];
           const bf16 a0 = (bf16)f0, a1 = (bf16)f1;
           const bf16 b0 = (bf16)(f0 - (float)a0), b1 = (bf16)(f1 - (float)a1);
           hv[h2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
