@@ -82,7 +82,8 @@ typedef enum {
     MORE_ERR_UNSUPPORTED = 7, /* outside the envelope: h % 8, r % 16, r > 128    */
     MORE_ERR_HIP = 8,         /* a HIP launch or query failed                    */
     MORE_ERR_ALIGNMENT = 9,   /* a tensor pointer is not 16-byte aligned         */
-    MORE_ERR_STALLED = 10     /* a kernel's bounded wait gave up: outputs invalid */
+    MORE_ERR_STALLED = 10,    /* a kernel's bounded wait gave up: outputs invalid */
+    MORE_ERR_SCRATCH_LIMIT = 11 /* needs more than the library's static scratch   */
 } more_status;
 
 typedef enum {
@@ -203,6 +204,25 @@ more_status more_dispatch_sort(const int32_t* topk_idx, int64_t N, int32_t k, in
 /* Workspace bytes of more_dispatch_sort (0 for arguments it rejects).  Pure
  * host function, no HIP call. */
 size_t more_dispatch_workspace_bytes(int64_t N, int32_t k, int64_t M);
+
+/*
+ * more_dispatch_sort for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, checks and results as more_dispatch_sort,
+ * without the workspace.  Its scratch (the per-block digit counts and the
+ * key + slot buffer of the multi-pass sort) is a static 32 MiB device array
+ * of the library, one per GPU, held until the process ends; no call here
+ * allocates or frees memory.  A call whose more_dispatch_workspace_bytes(N,
+ * k, M) exceeds 32 MiB (N k above about 4.1 million entries for M > 64)
+ * returns MORE_ERR_SCRATCH_LIMIT and enqueues nothing.  Every call on one
+ * GPU uses that GPU's one array and leaves it overwritten: calls that may
+ * overlap on one GPU (different streams, or threads without ordering) race
+ * and must be serialised by the caller.  MORE_ERR_HIP if the array's device
+ * address cannot be obtained.
+ */
+more_status more_dispatch_sort_noalloc(const int32_t* topk_idx, int64_t N, int32_t k, int64_t M,
+                                       int32_t* sorted_expert, int32_t* sorted_slot, int32_t* offsets,
+                                       void* stream);
 
 /*
  * Backward pass of the low-rank router with recompute (App. F.2.2, eq. (10)-

@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "more_route.h"
 #include "more_device.h"
@@ -389,6 +390,7 @@ const char* more_status_str(more_status s) {
     case MORE_ERR_HIP: return "HIP launch failed";
     case MORE_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
     case MORE_ERR_STALLED: return "a routing kernel's bounded wait gave up (outputs invalid)";
+    case MORE_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the library's static buffer holds";
   }
   return "unknown status";
 }
@@ -807,9 +809,21 @@ size_t more_dispatch_workspace_bytes(int64_t N, int32_t k, int64_t M) {
   return bytes;
 }
 
-more_status more_dispatch_sort(const int32_t* topk_idx, int64_t N, int32_t k, int64_t M, int32_t* sorted_expert,
-                               int32_t* sorted_slot, int32_t* offsets, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+}  // extern "C"
+
+// Scratch of more_dispatch_sort_noalloc: a file-scope device array (one copy
+// on every GPU the library runs on, held until the process ends).  Host code
+// must not pass its name to a kernel (on the host it is a stand-in, not a
+// device address): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in g_noalloc_ptr.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Argument checks shared by both dispatch-sort entry points (no HIP call).
+more_status dispatch_sort_check(const int32_t* topk_idx, int64_t N, int32_t k, int64_t M, const int32_t* sorted_expert,
+                                const int32_t* sorted_slot, const int32_t* offsets) {
   if (N < 0 || M < 1 || M > (1 << 24)) return MORE_ERR_BAD_SHAPE;
   if (k < 1 || (int64_t)k > M) return MORE_ERR_BAD_K;
   if (N * (int64_t)k >= ((int64_t)1 << 31) - 1) return MORE_ERR_BAD_SHAPE;
@@ -817,11 +831,14 @@ more_status more_dispatch_sort(const int32_t* topk_idx, int64_t N, int32_t k, in
   if (!topk_idx || !sorted_expert || !sorted_slot || !offsets) return MORE_ERR_NULL_ARG;
   if (!aligned16(topk_idx) || !aligned16(sorted_expert) || !aligned16(sorted_slot) || !aligned16(offsets))
     return MORE_ERR_ALIGNMENT;
-  const size_t need = more_dispatch_workspace_bytes(N, k, M);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0) return MORE_ERR_WORKSPACE;
+  return MORE_OK;
+}
+
+// The sort itself on a checked call; ws holds more_dispatch_workspace_bytes(N, k, M) bytes.
+more_status dispatch_sort_run(const int32_t* topk_idx, int64_t N, int32_t k, int64_t M, int32_t* sorted_expert,
+                              int32_t* sorted_slot, int32_t* offsets, char* ws, hipStream_t stream) {
   const int n = (int)(N * k);
   const int64_t B = (n + kSortBlock - 1) / kSortBlock;
-  char* ws = (char*)workspace;
   int* hist = (int*)ws;
   int* tk = nullptr;
   int* tv = nullptr;
@@ -830,8 +847,53 @@ more_status more_dispatch_sort(const int32_t* topk_idx, int64_t N, int32_t k, in
     tk = (int*)(ws + off);
     tv = (int*)(ws + off + align_up((size_t)n * sizeof(int)));
   }
-  return launch_dispatch_sort(topk_idx, n, (int)M, sorted_expert, sorted_slot, offsets, hist, tk, tv,
-                              (hipStream_t)stream) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+  return launch_dispatch_sort(topk_idx, n, (int)M, sorted_expert, sorted_slot, offsets, hist, tk, tv, stream) ==
+                 hipSuccess
+             ? MORE_OK
+             : MORE_ERR_HIP;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch copy, or nullptr on a HIP error.
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> guard(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_noalloc_ptr[dev] = p;
+  }
+  return g_noalloc_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+more_status more_dispatch_sort(const int32_t* topk_idx, int64_t N, int32_t k, int64_t M, int32_t* sorted_expert,
+                               int32_t* sorted_slot, int32_t* offsets, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const more_status c = dispatch_sort_check(topk_idx, N, k, M, sorted_expert, sorted_slot, offsets);
+  if (c != MORE_OK || N == 0) return c;
+  const size_t need = more_dispatch_workspace_bytes(N, k, M);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0) return MORE_ERR_WORKSPACE;
+  return dispatch_sort_run(topk_idx, N, k, M, sorted_expert, sorted_slot, offsets, (char*)workspace,
+                           (hipStream_t)stream);
+}
+
+more_status more_dispatch_sort_noalloc(const int32_t* topk_idx, int64_t N, int32_t k, int64_t M,
+                                       int32_t* sorted_expert, int32_t* sorted_slot, int32_t* offsets,
+                                       void* stream) {
+  const more_status c = dispatch_sort_check(topk_idx, N, k, M, sorted_expert, sorted_slot, offsets);
+  if (c != MORE_OK || N == 0) return c;
+  if (more_dispatch_workspace_bytes(N, k, M) > kNoAllocScratchBytes) return MORE_ERR_SCRATCH_LIMIT;
+  char* ws = (char*)noalloc_scratch();
+  if (!ws) return MORE_ERR_HIP;
+  return dispatch_sort_run(topk_idx, N, k, M, sorted_expert, sorted_slot, offsets, ws, (hipStream_t)stream);
 }
 
 more_status more_topk_merge(int64_t N, int64_t M, int64_t shard_width, int32_t k, more_gate gate,

@@ -21,13 +21,16 @@ MORE_ERR_WORKSPACE = 6
 MORE_ERR_UNSUPPORTED = 7
 STATUS_NAMES = {0: "MORE_OK", 1: "MORE_ERR_NULL_ARG", 2: "MORE_ERR_BAD_SHAPE", 3: "MORE_ERR_BAD_K",
                 4: "MORE_ERR_BAD_DTYPE", 5: "MORE_ERR_BAD_GATE", 6: "MORE_ERR_WORKSPACE",
-                7: "MORE_ERR_UNSUPPORTED", 8: "MORE_ERR_HIP", 9: "MORE_ERR_ALIGNMENT", 10: "MORE_ERR_STALLED"}
+                7: "MORE_ERR_UNSUPPORTED", 8: "MORE_ERR_HIP", 9: "MORE_ERR_ALIGNMENT", 10: "MORE_ERR_STALLED",
+                11: "MORE_ERR_SCRATCH_LIMIT"}
 MORE_ERR_STALLED = 10
+MORE_ERR_SCRATCH_LIMIT = 11
 EXPORTS = ("more_route_lowrank", "more_route_fullrank", "more_route_workspace_bytes",
            "more_status_str", "more_abi_version", "more_lowrank_pack", "more_lowrank_route_packed",
            "more_lowrank_balance_packed", "more_balance_workspace_bytes", "more_dispatch_sort",
            "more_dispatch_workspace_bytes", "more_lowrank_backward_packed", "more_backward_workspace_bytes",
-           "more_topk_merge", "more_set_route_paths", "more_route_status", "more_set_spin_limit")
+           "more_topk_merge", "more_set_route_paths", "more_route_status", "more_set_spin_limit",
+           "more_dispatch_sort_noalloc")
 
 _lock = threading.Lock()
 _lib = None
@@ -66,6 +69,8 @@ def lib() -> C.CDLL:
             L.more_balance_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i32]
             L.more_dispatch_sort.argtypes = [p, i64, i32, i64, p, p, p, p, C.c_size_t, p]
             L.more_dispatch_sort.restype = C.c_int
+            L.more_dispatch_sort_noalloc.argtypes = [p, i64, i32, i64, p, p, p, p]
+            L.more_dispatch_sort_noalloc.restype = C.c_int
             L.more_dispatch_workspace_bytes.argtypes = [i64, i32, i64]
             L.more_lowrank_backward_packed.argtypes = [i32, p, i64, i64, p, i64, p, i64, i32, p, p, p, p,
                                                        p, p, p, p, p, C.c_size_t, p]
@@ -265,6 +270,21 @@ def dispatch_sort(idx, M: int, *, out=None, workspace=None, stream=None) -> dict
     _check("more_dispatch_sort", lib().more_dispatch_sort(
         _ptr(idx), N, k, M, _ptr(out["sorted_expert"]), _ptr(out["sorted_slot"]), _ptr(out["offsets"]),
         _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def dispatch_sort_noalloc(idx, M: int, *, out=None, stream=None) -> dict:
+    """more_dispatch_sort_noalloc: as dispatch_sort, with the library's static
+    scratch instead of a workspace (outputs allocated here unless given)."""
+    import torch
+    N, k = idx.shape
+    if out is None:
+        out = dict(sorted_expert=torch.empty((N * k,), dtype=torch.int32, device=idx.device),
+                   sorted_slot=torch.empty((N * k,), dtype=torch.int32, device=idx.device),
+                   offsets=torch.empty((M + 1,), dtype=torch.int32, device=idx.device))
+    _check("more_dispatch_sort_noalloc", lib().more_dispatch_sort_noalloc(
+        _ptr(idx), N, k, M, _ptr(out["sorted_expert"]), _ptr(out["sorted_slot"]), _ptr(out["offsets"]),
+        _stream(stream)))
     return out
 
 

@@ -183,6 +183,20 @@ def test_dispatch_workspace_and_validation():
     assert f(FAKE, -1, 4, 64, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 2
 
 
+def test_dispatch_noalloc_rejects_before_any_hip_call():
+    """The allocation-free sort checks its arguments like more_dispatch_sort,
+    then its 32 MiB static scratch, before any HIP call."""
+    f = R.lib().more_dispatch_sort_noalloc
+    assert f(FAKE, 10, 4, 2, FAKE, FAKE, FAKE, None) == 3                   # k > M
+    assert f(None, 10, 4, 64, FAKE, FAKE, FAKE, None) == 1
+    assert f(ODD, 10, 4, 64, FAKE, FAKE, FAKE, None) == 9
+    assert f(FAKE, 0, 4, 64, None, None, None, None) == 0                   # N = 0: no-op
+    assert f(FAKE, -1, 4, 64, FAKE, FAKE, FAKE, None) == 2
+    assert R.dispatch_workspace_bytes(1 << 19, 8, 4096) > 32 << 20
+    assert f(FAKE, 1 << 19, 8, 4096, FAKE, FAKE, FAKE, None) == R.MORE_ERR_SCRATCH_LIMIT
+    assert R.status_str(R.MORE_ERR_SCRATCH_LIMIT) != "unknown status"
+
+
 def call_backward(dt=0, N=64, h=256, r=32, M=4096, k=8, idx=FAKE, tv=FAKE, pb=None, lse=FAKE, xg=FAKE,
                   r1g=FAKE, r2g=FAKE, bg=None, ws=FAKE, ws_bytes=100):
     return R.lib().more_lowrank_backward_packed(dt, FAKE, N, h, FAKE, r, FAKE, M, k, idx, tv, pb, lse, xg, r1g, r2g,
