@@ -140,10 +140,116 @@ __global__ __launch_bounds__(256) void merge_vec_kernel(MergeArgs a) {
   if (FULL && a.out_lse) a.out_lse[n] = lse;
 }
 
+// Many shards (G >= 32): one wave per token.  Lane l merges shards l, l + 64,
+// ... into its own ordered list; then k rounds each take the best head over
+// the wave (logit desc, index asc) and pop it from its lane.  The
+// full-softmax normaliser combines the lanes' shard values with a butterfly
+// (eq. (8)); the order of every sum is fixed.
+template <int KMAX, bool FULL>
+__global__ __launch_bounds__(256) void merge_wave_kernel(MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= a.N) return;   // wave-uniform
+  float V[KMAX];
+  int IX[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    V[j] = -__builtin_inff();
+    IX[j] = 0x7fffffff;
+  }
+  float m = -__builtin_inff(), Z = 0.f;
+  for (int g = lane; g < a.G; g += kWave) {
+    const size_t base = ((size_t)g * a.N + n) * a.k;
+    const long long off = (long long)g * a.W;
+    // the shard's whole list first (its loads in flight together), then the inserts
+    float cl[KMAX];
+    int ci[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      cl[j] = j < a.k ? a.cand_logit[base + j] : -__builtin_inff();
+      ci[j] = j < a.k ? a.cand_idx[base + j] : 0x7fffffff;
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (cl[j] >= V[KMAX - 1]) ordered_insert<KMAX>(V, IX, cl[j], (int)(off + ci[j]));
+    if (FULL) {
+      const float l = a.shard_lse[(size_t)g * a.N + n];
+      const float mn = fmaxf(m, l);
+      Z = Z * __builtin_amdgcn_exp2f((m - mn) * kLog2e) + __builtin_amdgcn_exp2f((l - mn) * kLog2e);
+      m = mn;
+    }
+  }
+  float lse = 0.f;
+  if (FULL) {
+    float mm = m;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
+    float z = m > -__builtin_inff() ? Z * __builtin_amdgcn_exp2f((m - mm) * kLog2e) : 0.f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
+    lse = mm + __builtin_amdgcn_logf(z) * kLn2;
+  }
+  // k rounds: the wave's best head, popped from the lane that holds it
+  float rv = -__builtin_inff();   // lane j keeps round j's logit and index
+  int ri = 0x7fffffff;
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) {
+    if (r < a.k) {
+      float v = V[0];
+      int i = IX[0];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float v2 = __shfl_xor(v, o);
+        const int i2 = __shfl_xor(i, o);
+        const bool better = v2 > v || (v2 == v && i2 < i);
+        v = better ? v2 : v;
+        i = better ? i2 : i;
+      }
+      if (lane == r) {
+        rv = v;
+        ri = i;
+      }
+      const bool pop = V[0] == v && IX[0] == i;
+#pragma unroll
+      for (int j = 0; j + 1 < KMAX; ++j) {
+        V[j] = pop ? V[j + 1] : V[j];
+        IX[j] = pop ? IX[j + 1] : IX[j];
+      }
+      if (pop) {
+        V[KMAX - 1] = -__builtin_inff();
+        IX[KMAX - 1] = 0x7fffffff;
+      }
+    }
+  }
+  // gates: round 0 holds the best logit
+  const float v0 = __shfl(rv, 0);
+  const float w = lane < a.k ? __builtin_amdgcn_exp2f((rv - (FULL ? lse : v0)) * kLog2e) : 0.f;
+  float denom = w;
+  if (!FULL) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) denom += __shfl_xor(denom, o);
+  }
+  if (lane < a.k) {
+    const size_t o = (size_t)n * a.k + lane;
+    a.out_idx[o] = ri;
+    a.out_gate[o] = FULL ? w : w / denom;
+    if (a.out_logit) a.out_logit[o] = rv;
+  }
+  if (FULL && a.out_lse && lane == 0) a.out_lse[n] = lse;
+}
+
 static bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; }
 
 template <int KMAX>
 static hipError_t launch_k(const MergeArgs& a, bool full, hipStream_t s) {
+  if (a.G >= 32 && a.N <= (1LL << 30)) {
+    const dim3 wgrid((unsigned)((a.N + 3) / 4));
+    if (full)
+      hipLaunchKernelGGL((merge_wave_kernel<KMAX, true>), wgrid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((merge_wave_kernel<KMAX, false>), wgrid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((a.N + 255) / 256));
   if constexpr (KMAX <= 16) {   // larger lists spill in the 16-byte form
     const bool vec = a.k == KMAX && aligned16(a.cand_logit) && aligned16(a.cand_idx) && aligned16(a.out_idx) &&

@@ -8,6 +8,7 @@
 #include "more_pc.h"
 #include "more_split.h"
 #include "more_sweep.h"
+#include "more_splitm.h"
 
 namespace more {
 
@@ -86,6 +87,33 @@ constexpr int kSwCons = 8;   // consumer waves (+ kSwLoaders loaders), one workg
 sweep_fn pick_sweep(bool full, bool lse, int kmax, int r16);
 size_t sweep_lds_bytes(int kmax, int r16);
 
+
+// Split-M form (few tokens, many experts): bf16, r <= 128, any k.
+typedef void (*splitm_proj_fn)(SplitmProjArgs);
+typedef void (*splitm_fn)(SplitmArgs);
+constexpr int kSplitmMaxBlocks = 64;   // used for at most 64 blocks of 32 tokens
+constexpr int kSplitmWaves = 1024;     // routing waves aimed at (blocks x shards)
+splitm_proj_fn pick_splitm_proj(int r16);
+splitm_fn pick_splitm_topk(int kmax, int r16);
+splitm_fn pick_splitm_full(int kmax, int r16);
+template <bool FULL, int KMAX>
+splitm_fn pick_splitm_r(int r16) {
+  switch (r16) {
+    case 1: return splitm_route_kernel<KMAX, FULL, 1>;
+    case 2: return splitm_route_kernel<KMAX, FULL, 2>;
+    case 4: return splitm_route_kernel<KMAX, FULL, 4>;
+    default: return splitm_route_kernel<KMAX, FULL, 8>;
+  }
+}
+template <bool FULL>
+splitm_fn pick_splitm_k(int kmax, int r16) {
+  switch (kmax) {
+    case 4: return pick_splitm_r<FULL, 4>(r16);
+    case 8: return pick_splitm_r<FULL, 8>(r16);
+    case 16: return pick_splitm_r<FULL, 16>(r16);
+    default: return pick_splitm_r<FULL, 32>(r16);
+  }
+}
 
 lowrank_fn pick_lowrank_bf16_topk(int kmax, int r16);
 lowrank_fn pick_lowrank_bf16_full(int kmax, int r16);

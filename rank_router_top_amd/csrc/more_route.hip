@@ -114,6 +114,52 @@ size_t z_scratch_bytes(more_dtype dt, const Layout& L, int64_t N) {
   return align_up((size_t)nb * (size_t)z_block_bytes(L.r16));
 }
 
+// Split-M form (few tokens, many experts): shards of the sweep tiles and the
+// token scratch behind the packed weights.
+struct SplitmPlan {
+  int NB, S, TPS, KS, KPS;
+  size_t off_part, off_cl, off_ci, off_cg, off_lse, bytes;   // offsets from the scratch start
+};
+
+bool splitm_plan(more_dtype dt, const Layout& L, int64_t N, int64_t h, int k, SplitmPlan* P) {
+  if (dt != MORE_DT_BF16 || N <= 0 || L.r16 > 8) return false;
+  const int64_t nb = (N + kTile - 1) / kTile;
+  if (nb > kSplitmMaxBlocks) return false;
+  // about kSplitmWaves routing waves; shards of a multiple of 4 tiles (so
+  // every shard holds a real expert: padding is confined to the last 4 tiles)
+  const int64_t want = std::min<int64_t>(std::max<int64_t>(kSplitmWaves / nb, 1), L.NT / 4);
+  if (want < 4) return false;
+  const int64_t tps = ((L.NT + want - 1) / want + 3) / 4 * 4;
+  P->NB = (int)nb;
+  P->TPS = (int)tps;
+  P->S = (int)((L.NT + tps - 1) / tps);
+  P->KS = (int)((h + 15) / 16);
+  P->KPS = (P->KS + kSplitmKParts - 1) / kSplitmKParts;
+  const int rb = (L.r16 + 1) / 2;
+  const size_t cand = align_up((size_t)P->S * (size_t)N * (size_t)k * 4);
+  size_t off = 0;
+  P->off_part = off;
+  off += align_up((size_t)kSplitmKParts * (size_t)nb * rb * 16 * kWave * sizeof(float));
+  P->off_cl = off;
+  off += cand;
+  P->off_ci = off;
+  off += cand;
+  P->off_cg = off;
+  off += cand;
+  P->off_lse = off;
+  off += align_up((size_t)P->S * (size_t)N * sizeof(float));
+  P->bytes = off;
+  return true;
+}
+
+// Token scratch of a routing call: z for the two-kernel form, or the
+// split-M form's partial sums and shard candidates.
+size_t token_scratch_bytes(more_dtype dt, const Layout& L, int64_t N, int64_t h, int k) {
+  SplitmPlan P;
+  const size_t sm = splitm_plan(dt, L, N, h, k, &P) ? P.bytes : 0;
+  return std::max(z_scratch_bytes(dt, L, N), sm);
+}
+
 // Workspace of the balancing call: packed weights, z scratch for N tokens,
 // then the per-slot partial column sums (fp32, by sweep position) and the
 // per-slot counts (int32, by expert).  Returns false outside its envelope
@@ -149,17 +195,18 @@ more_status validate(int fullrank, more_dtype dt, const void* X, int64_t N, int6
 // Kernel paths of the low-rank router, in the order they are tried (measured
 // fastest first on the workloads they share).  Each call takes the first one
 // whose shape envelope fits.  A testing aid can restrict the candidates to a
-// subset of "split,ring,pc,lock,stream" (the plain kernel always remains, so that
+// subset of "split,ring,splitm,pc,lock,stream" (the plain kernel always remains, so that
 // every path can be checked on the shapes a faster one would take): the
 // environment variable MORE_ROUTE_PATHS, read once at the first routing call,
 // or more_set_route_paths() at any time.
-enum { kPathPc = 1, kPathLock = 4, kPathStream = 8, kPathSplit = 16, kPathRing = 32, kPathAll = 63 };
+enum { kPathPc = 1, kPathLock = 4, kPathStream = 8, kPathSplit = 16, kPathRing = 32, kPathSplitM = 64, kPathAll = 127 };
 
 int parse_paths(const char* names) {
   if (!names || !*names) return kPathAll;
   int mask = 0;
   static const struct { const char* name; int bit; } table[] = {
-      {"split", kPathSplit}, {"ring", kPathRing}, {"pc", kPathPc}, {"lock", kPathLock}, {"stream", kPathStream}};
+      {"split", kPathSplit}, {"ring", kPathRing}, {"splitm", kPathSplitM}, {"pc", kPathPc}, {"lock", kPathLock},
+      {"stream", kPathStream}};
   for (const char* p = names; *p;) {
     const char* e = strchr(p, ',');
     const size_t n = e ? (size_t)(e - p) : strlen(p);
@@ -199,6 +246,54 @@ bool split_fits(int kmax, const Layout& L, int64_t h, bool ring) {
 // Two kernels: projection (R1 resident in LDS) writes z of every 32-token
 // block to the token scratch behind the packed weights, routing sweeps it.
 // lse_mode: pass 1 covers every tile and lse is written (implied by full).
+// Split-M form: projection in K-parts, one wave per (block, shard), then the
+// merge of the shards' candidate lists.
+more_status launch_splitm(const LowRankArgs& a, const Layout& L, const SplitmPlan& P, int kmax, bool full,
+                          char* scratch, hipStream_t stream) {
+  SplitmProjArgs pa;
+  pa.X = a.X;
+  pa.N = a.N;
+  pa.h = a.h;
+  pa.NB = P.NB;
+  pa.KS = P.KS;
+  pa.KPS = P.KPS;
+  pa.R1p = a.R1p;
+  pa.part = (float*)(scratch + P.off_part);
+  hipLaunchKernelGGL(pick_splitm_proj(L.r16), dim3((unsigned)(P.NB * kSplitmKParts)), dim3(64), 0, stream, pa);
+  if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
+  SplitmArgs sa;
+  sa.base = a;
+  sa.part = pa.part;
+  sa.NB = P.NB;
+  sa.TPS = P.TPS;
+  sa.S = P.S;
+  sa.cand_logit = (float*)(scratch + P.off_cl);
+  sa.cand_idx = (int*)(scratch + P.off_ci);
+  sa.cand_gate = (float*)(scratch + P.off_cg);
+  sa.shard_lse = full ? (float*)(scratch + P.off_lse) : nullptr;
+  splitm_fn rf = full ? pick_splitm_full(kmax, L.r16) : pick_splitm_topk(kmax, L.r16);
+  const size_t lds = 4 * log_bytes(kmax);
+  if (hipFuncSetAttribute((const void*)rf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return MORE_ERR_HIP;
+  const int rw = P.NB * P.S;
+  hipLaunchKernelGGL(rf, dim3((unsigned)((rw + 3) / 4)), dim3(256), lds, stream, sa);
+  if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
+  // the candidates carry global expert indices: shard offset 0
+  MergeArgs m;
+  m.cand_logit = sa.cand_logit;
+  m.cand_idx = sa.cand_idx;
+  m.shard_lse = sa.shard_lse;
+  m.out_idx = a.out_idx;
+  m.out_gate = a.out_gate;
+  m.out_logit = a.out_logit;
+  m.out_lse = a.out_lse;
+  m.N = a.N;
+  m.W = 0;
+  m.G = P.S;
+  m.k = a.k;
+  return launch_topk_merge(m, full, stream) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
+}
+
 more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int kmax, bool full, bool lse_mode,
                          bool ring, char* ws, hipStream_t stream) {
   int ksp = 0;
@@ -408,7 +503,7 @@ size_t more_route_workspace_bytes(int fullrank, more_dtype dt, int64_t N, int64_
   if (N < 0) return 0;
   if (fullrank && dt == MORE_DT_BF16 && fr_tiled_supported(h, M, k))
     return std::max(L.total, align_up(fr_tiled_bytes(h, M)));
-  return L.total + (fullrank ? 0 : z_scratch_bytes(dt, L, N));
+  return L.total + (fullrank ? 0 : token_scratch_bytes(dt, L, N, h, k));
 }
 
 more_status more_lowrank_pack(more_dtype dt, const void* R1, int64_t h, int64_t r, const void* R2,
@@ -458,6 +553,10 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   a.out_logit = topk_logit;
   a.out_lse = full ? lse : nullptr;
   const size_t shmem = (size_t)waves * log_bytes(kmax);
+  SplitmPlan sp;
+  if (path_allowed(kPathSplitM) && splitm_plan(dt, L, N, h, k, &sp) && workspace_bytes >= L.total + sp.bytes &&
+      4 * log_bytes(kmax) <= (size_t)kLdsBytes)
+    return launch_splitm(a, L, sp, kmax, full, ws + L.total, (hipStream_t)stream);
   const size_t zbytes = z_scratch_bytes(dt, L, N);
   if (zbytes > 0 && workspace_bytes >= L.total + zbytes) {
     if (path_allowed(kPathSplit) && split_fits(kmax, L, h, false))

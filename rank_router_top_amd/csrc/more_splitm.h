@@ -1,0 +1,212 @@
+// more_splitm.h -- the low-rank router for few tokens and many experts
+// (decode): the expert range is split over many waves.
+//
+// Method: "MoRE: Scaling mixture of experts with hardware-aware low-rank
+// routing", App. F.1 Algorithm 1 (z = X-block times the down-projection, then
+// a sweep over the experts with a running top-k) and App. E.3 (a top-k over
+// shards of the experts, merged; the full-softmax normaliser combined across
+// shards by eq. (8)).
+//
+// With N = 256 tokens there are 8 blocks of 32: one wave per block leaves
+// almost the whole GPU idle while each wave sweeps M = 65536 experts.  Here
+//   splitm_proj_kernel   wave (block, K-part): z of the block over an eighth
+//                        of the hidden units (fp32 partial sums);
+//   splitm_route_kernel  wave (block, shard): z = the sum of the partials, in
+//                        a fixed order; then the exact two-half sweep of
+//                        more_lowrank.h over the shard's expert tiles only,
+//                        finished as the shard's k best (logit, expert) and
+//                        its log-sum-exp;
+//   merge_kernel         (more_merge.h) the k best of the shards' lists, and
+//                        the gates.
+// Shards are ranges of sweep tiles (at least 4 tiles each, so every shard
+// holds a real expert); the candidates carry global expert indices.
+#pragma once
+#include "more_device.h"
+#include "more_lowrank.h"
+
+namespace more {
+
+constexpr int kSplitmKParts = 8;   // K-parts of the projection
+
+struct SplitmProjArgs {
+  const void* X;
+  long long N;
+  int h;
+  int NB;            // 32-token blocks
+  int KS;            // 16-column K-steps of h
+  int KPS;           // K-steps per part
+  const void* R1p;   // packed down-projection (A operands of the 32x32x16 MFMA)
+  float* part;       // [kSplitmKParts][NB][RB][16][64 lanes] fp32
+};
+
+// one wave per workgroup (spread over the CUs): block b = wg / kSplitmKParts,
+// part p = wg % kSplitmKParts
+template <int R16>
+__global__ __launch_bounds__(64) void splitm_proj_kernel(SplitmProjArgs a) {
+  constexpr int RB = (R16 + 1) / 2;
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / kSplitmKParts, p = blockIdx.x % kSplitmKParts;
+  const bool hi = lane >= 32;
+  const int hf = hi ? 1 : 0, col = lane & 31;
+  const long long n = (long long)b * kTile + col;
+  const long long row = n < a.N ? n : a.N - 1;
+  const uint16_t* xrow = (const uint16_t*)a.X + (size_t)row * a.h;
+  const bf16x8* r1p = (const bf16x8*)a.R1p;
+  floatx16 z[RB];
+#pragma unroll
+  for (int q = 0; q < RB; ++q)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) z[q][v] = 0.f;
+  const int s0 = p * a.KPS, s1 = min(s0 + a.KPS, a.KS);
+  // groups of 4 K-steps, the next group's loads in flight while one is
+  // multiplied (clamped K-steps past the part re-read its last one; their
+  // products are skipped)
+  constexpr int U = 4;
+  auto xaddr = [&](int s) {
+    const int c = (16 * s + 8 * hf < a.h) ? 16 * s + 8 * hf : 16 * s;   // a half-filled last K-step
+    return (const bf16x8*)(xrow + c);
+  };
+  auto load = [&](int s, bf16x8 (&xs)[U], bf16x8 (&rs)[U][RB]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sc = min(s + u, s1 - 1);
+      xs[u] = __builtin_nontemporal_load(xaddr(sc));
+#pragma unroll
+      for (int q = 0; q < RB; ++q) rs[u][q] = r1p[((size_t)sc * RB + q) * kWave + lane];
+    }
+  };
+  auto compute = [&](int s, const bf16x8 (&xs)[U], const bf16x8 (&rs)[U][RB]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s + u < s1) {
+#pragma unroll
+        for (int q = 0; q < RB; ++q) z[q] = mfma_bf16(rs[u][q], xs[u], z[q]);
+      }
+  };
+  if (s0 < s1) {
+    bf16x8 xa[U], ra[U][RB], xb[U], rb[U][RB];
+    load(s0, xa, ra);
+    int s = s0;
+    for (; s + U < s1; s += 2 * U) {
+      load(s + U, xb, rb);
+      compute(s, xa, ra);
+      load(min(s + 2 * U, s1 - 1), xa, ra);
+      compute(s + U, xb, rb);
+    }
+    if (s < s1) compute(s, xa, ra);
+  }
+  float* dst = a.part + ((size_t)p * a.NB + b) * RB * 16 * kWave;
+#pragma unroll
+  for (int q = 0; q < RB; ++q)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dst[((size_t)q * 16 + v) * kWave + lane] = z[q][v];
+}
+
+struct SplitmArgs {
+  LowRankArgs base;     // N, NT, k, R2p, biasq, perm (outputs unused)
+  const float* part;    // from splitm_proj_kernel
+  int NB;               // 32-token blocks
+  int TPS;              // tiles per shard (>= 4; the last shard may be shorter)
+  int S;                // shards
+  float* cand_logit;    // [S][N][k]
+  int* cand_idx;        // [S][N][k] global expert indices
+  float* cand_gate;     // [S][N][k] scratch (the per-shard gates are not used)
+  float* shard_lse;     // [S][N] (full-softmax gate) or null
+};
+
+// wave (block b, shard s) = global wave index s * NB + b (the blocks of one
+// shard are neighbours: they share the shard's R2 tiles in L2)
+template <int KMAX, bool FULL, int R16>
+__global__ __launch_bounds__(256) void splitm_route_kernel(SplitmArgs sa) {
+  const LowRankArgs& a = sa.base;
+  constexpr int CAP = Cap<KMAX>::value;
+  constexpr int RB = (R16 + 1) / 2;
+  extern __shared__ float2 smem_log[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gw = blockIdx.x * 4 + wave;
+  if (gw >= sa.NB * sa.S) return;   // wave-uniform
+  const int s = gw / sa.NB, b = gw % sa.NB;
+  const bool hi = lane >= 32;
+  const int hf = hi ? 1 : 0, col = lane & 31;
+  const long long n = (long long)b * kTile + col;
+  const bool rowok = n < a.N;
+  LogRef lg{smem_log + (size_t)wave * CAP * kWave};
+
+  // z of the block: the K-parts summed in a fixed order
+  floatx16 z[RB];
+#pragma unroll
+  for (int q = 0; q < RB; ++q)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) z[q][v] = 0.f;
+  for (int p = 0; p < kSplitmKParts; ++p) {
+    const float* src = sa.part + ((size_t)p * sa.NB + b) * RB * 16 * kWave;
+#pragma unroll
+    for (int q = 0; q < RB; ++q)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) z[q][v] += src[((size_t)q * 16 + v) * kWave + lane];
+  }
+  bf16x8 zh[R16], zl[R16];
+#pragma unroll
+  for (int m = 0; m < R16; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = z[m >> 1][8 * (m & 1) + e];
+      const bf16 hv = (bf16)f;
+      zh[m][e] = hv;
+      zl[m][e] = (bf16)(f - (float)hv);
+    }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)((!hi && e < 2) ? 1.f : 0.f);
+  const bf16x8* r2p = (const bf16x8*)a.R2p;
+  const uint32_t* bq = a.biasq;
+  const int t0 = s * sa.TPS, t1 = min(t0 + sa.TPS, a.NT);
+  struct Ops {
+    bf16x8 w[R16];
+    uint32_t b;
+  };
+  auto load_ops = [&](int t, Ops& o) {
+    const int tc = t < t1 ? t : t1 - 1;   // clamped: always a tile of the shard
+#pragma unroll
+    for (int m = 0; m < R16; ++m) o.w[m] = r2p[((size_t)tc * R16 + m) * kWave + lane];
+    o.b = bq[(size_t)tc * kWave + lane];
+  };
+  auto logits = [&](const Ops& o) {
+    bf16x8 ab;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ab[e] = (bf16)0.f;
+    ab[0] = __builtin_bit_cast(bf16, (uint16_t)(o.b & 0xffffu));
+    ab[1] = __builtin_bit_cast(bf16, (uint16_t)(o.b >> 16));
+    floatx16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    acc = mfma_bf16(ab, ones, acc);
+#pragma unroll
+    for (int m = 0; m < R16; ++m) acc = mfma_bf16(o.w[m], zh[m], acc);
+#pragma unroll
+    for (int m = 0; m < R16; ++m) acc = mfma_bf16(o.w[m], zl[m], acc);
+    return acc;
+  };
+  SweepState<KMAX, CAP> st;
+  st.init(a.k);
+  // two tiles in flight, as in lowrank_kernel
+  Ops o0, o1;
+  load_ops(t0, o0);
+  load_ops(t0 + 1, o1);
+  floatx16 accA = logits(o0);
+  load_ops(t0 + 2, o0);
+  for (int t = t0; t < t1; t += 2) {
+    floatx16 accB = logits(o1);
+    load_ops(t + 3, o1);
+    st.template tile<FULL>(accA, kTile * t + 4 * hf, lg, lane, hi, a.perm, a.k);
+    accA = logits(o0);   // beyond the shard's last tile: unused
+    load_ops(t + 4, o0);
+    if (t + 1 < t1) st.template tile<FULL>(accB, kTile * (t + 1) + 4 * hf, lg, lane, hi, a.perm, a.k);
+  }
+  const size_t so = (size_t)s * a.N;
+  finish_tokens<KMAX, CAP, FULL>(st, lg, lane, hi, rowok, n, a.perm, a.k, sa.cand_idx + so * a.k,
+                                 sa.cand_gate + so * a.k, sa.cand_logit + so * a.k,
+                                 FULL ? sa.shard_lse + so : nullptr);
+}
+
+}  // namespace more

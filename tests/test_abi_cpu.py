@@ -47,7 +47,14 @@ def test_workspace_size_is_pure_host_and_rejects_bad_args():
     # plus token scratch: z of every 32-token block as bf16 hi + lo (4 bytes per token and rank)
     ws = R.workspace_bytes(False, R.MORE_DT_BF16, 262144, 2048, 32, 4096, 8, 0, True)
     assert ws == packed + 262144 * 32 * 4
-    assert R.workspace_bytes(False, R.MORE_DT_BF16, 33, 2048, 32, 4096, 8, 0, True) == packed + 2 * 32 * 128
+    # few tokens (at most 64 blocks of 32): the split-M form's scratch instead,
+    # when larger: 8 K-part partial sums of z (fp32, 4 KiB per block and 32
+    # ranks) and, per shard of 4 expert tiles (32 shards at M = 4096), k
+    # candidate logits, indices and gates and one log-sum-exp per token
+    parts = 8 * 2 * 4096
+    cand = 32 * 33 * 8 * 4
+    lse = (32 * 33 * 4 + 255) // 256 * 256
+    assert R.workspace_bytes(False, R.MORE_DT_BF16, 33, 2048, 32, 4096, 8, 0, True) == packed + parts + 3 * cand + lse
     assert R.workspace_bytes(False, R.MORE_DT_F32, 1000, 2048, 32, 4096, 8, 0, True) == \
         R.workspace_bytes(False, R.MORE_DT_F32, 0, 2048, 32, 4096, 8, 0, True)   # fp32: no two-kernel path
     assert ws % 256 == 0 and packed % 256 == 0
@@ -151,8 +158,9 @@ def test_balance_workspace_bytes():
     bf = R.MORE_DT_BF16
     route = R.workspace_bytes(False, bf, 262144, 2048, 32, 4096, 8, 0, True)
     assert R.balance_workspace_bytes(bf, 262144, 2048, 32, 4096, 8) == route + 2 * 256 * 4096 * 4
-    route33 = R.workspace_bytes(False, bf, 33, 2048, 32, 4096, 8, 0, True)
-    assert R.balance_workspace_bytes(bf, 33, 2048, 32, 4096, 8) == route33 + 2 * 2 * 4096 * 4
+    packed = R.workspace_bytes(False, bf, 0, 2048, 32, 4096, 8, 0, True)
+    # 33 tokens: z of 2 blocks (4 KiB each) and 2 partial-sum slots
+    assert R.balance_workspace_bytes(bf, 33, 2048, 32, 4096, 8) == packed + 2 * 4096 + 2 * 2 * 4096 * 4
     assert R.balance_workspace_bytes(bf, 10, 2048, 32, 65535, 8) > 0
     assert R.balance_workspace_bytes(bf, 10, 2048, 32, 65537, 8) == 0    # 16-bit sweep positions
     assert R.balance_workspace_bytes(bf, 10, 2048, 32, 65535, 4) > 0

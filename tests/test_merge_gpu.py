@@ -51,7 +51,9 @@ def sharded_route(X, R1, R2, b, k, gate, width):
     return {key: (None if v is None else v.cpu().numpy()) for key, v in out.items()}
 
 
-CASES = [(CF.HEADLINE, 1024 + 19, 512), (CF.HEADLINE, 700, 2048), (CF.PREFILL_H512, 900, 1000)]
+# the last two have 41 and 64 shards: the merge takes one wave per token there
+CASES = [(CF.HEADLINE, 1024 + 19, 512), (CF.HEADLINE, 700, 2048), (CF.PREFILL_H512, 900, 1000),
+         (CF.HEADLINE, 300, 100), (CF.HEADLINE, 200, 64)]
 
 
 @pytest.mark.parametrize("cfg,n,width", CASES, ids=[f"{c.name}-{n}-w{w}" for c, n, w in CASES])

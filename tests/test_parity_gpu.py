@@ -135,6 +135,31 @@ def test_edge_shapes(oracle_lib, N, h, r, M, k, dt):
                       logit_tol=2e-4 if dt == "bf16" else 1e-5)
 
 
+# Few tokens, many experts: the expert range split over (block, shard) waves and
+# the shards' candidate lists merged (App. E.3; eq. (8) across shards).  The
+# shapes cover one token, a ragged M with the largest k, the largest block
+# count the form takes (64 blocks), r = 128 and a shard whose tiles hold a
+# single real expert (M = 32 t + 1).
+@pytest.mark.parametrize("N,h,r,M,k", [
+    (1, 4096, 64, 65536, 16),
+    (100, 512, 32, 8192 + 5, 32),
+    (2048, 2048, 32, 4096, 8),
+    (300, 1024, 128, 20000, 4),
+    (77, 256, 16, 32 * 260 + 1, 8),
+])
+def test_splitm_shapes(oracle_lib, route_paths, N, h, r, M, k):
+    route_paths("splitm")
+    rng = np.random.default_rng(N * 3 + M)
+    X = rng.standard_normal((N, h))
+    X /= np.sqrt(np.mean(X * X, axis=1, keepdims=True))
+    R1 = rng.standard_normal((h, r)) / math.sqrt(h)
+    R2 = rng.standard_normal((r, M)) / math.sqrt(r)
+    b = (rng.standard_normal(M) * 0.7).astype(np.float32)
+    X, R1, R2 = (I.f32_to_bf16_bits(a.astype(np.float32)) for a in (X, R1, R2))
+    for gate in (0, 1):
+        check_lowrank(oracle_lib, X, R1, R2, b, k, gate, f"splitm-{N}x{h}x{r}x{M}-k{k}")
+
+
 def test_exact_ties_lower_index_wins(oracle_lib):
     """Duplicated R2 columns (and equal biases) give bitwise-equal logits; the
     lower expert index must win, with and without the bias-ordered sweep."""
@@ -269,7 +294,7 @@ def route_paths():
     R.set_route_paths(None)
 
 
-@pytest.mark.parametrize("path", ["split", "ring", "pc", "lock", "stream", "none"])
+@pytest.mark.parametrize("path", ["split", "ring", "splitm", "pc", "lock", "stream", "none"])
 @pytest.mark.parametrize("cfg,n,gate", PATH_CASES, ids=[f"{c.name}-{n}-g{g}" for c, n, g in PATH_CASES])
 def test_kernel_paths(oracle_lib, route_paths, path, cfg, n, gate):
     route_paths(path)
