@@ -39,6 +39,15 @@ resident in HBM.  Prints ONE JSON line:
                  timed, the merge against 8 TB/s over its algorithmic bytes,
                  plus the count of tokens whose merged selection differs
                  from the unsharded call
+  configs        the routing call (weights packed once) on the other
+                 workloads: prefill at h = 512 with both gates, r = 16, 64
+                 and 128 at the headline's shape, the many-expert prefill
+                 (N = 65536, h = 4096, M = 65536, r = 64, k = 16, full
+                 softmax) and its decode (N = 256); HIP-event timed, against
+                 the roofline max(algorithmic bytes / 8 TB/s, 2N(hr + rM) /
+                 2.5 PFLOP/s).  Tokens are generated on the device (seeded
+                 Gaussian rows, RMS-normalised, bf16: the same recipe); the
+                 r = 16/64/128 legs reuse the headline's tokens
   context        published B200 figures of the paper (other hardware)
 Only one GPU is supported: --gpus above 1 exits with a message.
 """
@@ -55,13 +64,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 # the kernels one routing call of the headline workload runs (rocprofv3 names)
-ROUTER_KERNELS = ("more::proj_kernel<2, 8, false, 4>", "more::route_kernel<8, false, 2, 8, false>")
+ROUTER_KERNELS = ("more::proj_kernel<2, 16, false, 4>", "more::route_kernel<8, false, 2, 8, false>")
 KERNEL_NAME = " + ".join(ROUTER_KERNELS)
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published (no sparsity)
 # v_exp_f32 rate: 256 CUs x 4 SIMDs x 16 lanes per cycle at half rate (one wave64
 # exp per 8 cycles, measured against v_fma_f32 at one per 4), 2.4 GHz
 EXP_PEAK_PER_S = 256 * 4 * 16 / 2 * 2.4e9
-BALANCE_KERNELS = ("more::proj_kernel<2, 8, false, 4>", "more::route_kernel<8, false, 2, 8, true>",
+BALANCE_KERNELS = ("more::proj_kernel<2, 16, false, 4>", "more::route_kernel<8, false, 2, 8, true>",
                    "more::psum_kernel<2, 8, 8>", "more::count_kernel", "more::colsum_kernel",
                    "more::stats_kernel")
 CONTEXT = {
@@ -92,6 +101,8 @@ def parse():
     ap.add_argument("--no-dispatch", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-sharded", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--configs-only", action="store_true", help="only the other workloads' legs")
     ap.add_argument("--shards", type=int, default=8)
     ap.add_argument("--fullrank-steps", type=int, default=3)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -211,6 +222,64 @@ def time_events(torch, fn, steps, stream):
     return sum(ms) / len(ms), ms[len(ms) // 2], ms[len(ms) // 10], ms[(9 * len(ms)) // 10]
 
 
+def device_tokens(torch, n, h, seed, dev):
+    """Seeded Gaussian rows, RMS-normalised, as bf16 on the device."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    x = torch.randn((n, h), generator=g, device=dev, dtype=torch.float32)
+    x = x * torch.rsqrt((x * x).mean(dim=1, keepdim=True))
+    return x.to(torch.bfloat16)
+
+
+CONFIG_LEGS = (("prefill_h512", 0), ("prefill_h512", 1), ("rank16", 0), ("rank64", 0), ("rank128", 0),
+               ("many_experts_prefill", 1), ("many_experts_decode", 1))
+
+
+def config_legs(args, torch, R, CF, dev, stream, X_headline):
+    """The routing call (packed weights) on the other workloads."""
+    out = {}
+    X_many = None
+    for name, gate in CONFIG_LEGS:
+        cfg = CF.ALL[name]
+        if name == "prefill_h512":
+            X = device_tokens(torch, cfg.N, cfg.h, 1000 + args.seed, dev)
+        elif name == "many_experts_prefill":
+            X_many = device_tokens(torch, cfg.N, cfg.h, 2000 + args.seed, dev)
+            X = X_many
+        elif name == "many_experts_decode":
+            X = X_many[:cfg.N] if X_many is not None else device_tokens(torch, cfg.N, cfg.h, 2000 + args.seed, dev)
+        else:
+            X = X_headline
+        R1, R2, b = (R.to_device(a, dev) for a in cfg.weights(args.seed))
+        nb = R.workspace_bytes(False, R.MORE_DT_BF16, cfg.N, cfg.h, cfg.r, cfg.M, cfg.k, gate, b is not None)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        R.pack_lowrank(R1, R2, b, ws, stream=stream)
+        o = dict(idx=torch.empty((cfg.N, cfg.k), dtype=torch.int32, device=dev),
+                 gate=torch.empty((cfg.N, cfg.k), dtype=torch.float32, device=dev),
+                 logit=None, lse=torch.empty((cfg.N,), dtype=torch.float32, device=dev) if gate else None)
+
+        def call():
+            R.route_lowrank_packed(X, cfg.r, cfg.M, cfg.k, gate, ws, out=o, stream=stream)
+
+        for _ in range(3):
+            call()
+        mean, med, p10, p90 = time_events(torch, call, 20, stream)
+        alg = algorithmic_bytes(cfg, cfg.k, gate == 1)
+        flops = cfg.flops()
+        t_hbm, t_mfma = alg / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+        roof = max(t_hbm, t_mfma)
+        key = f"{name}/{'full_softmax' if gate else 'topk_softmax'}"
+        out[key] = {"N": cfg.N, "h": cfg.h, "M": cfg.M, "r": cfg.r, "k": cfg.k, "bias": cfg.has_bias,
+                    "ms_per_call": mean, "ms_median": med, "ms_p10": p10, "ms_p90": p90,
+                    "tokens_per_s": cfg.N / (mean * 1e-3), "algorithmic_bytes": alg,
+                    "hbm_gbs": alg / (mean * 1e-3) / 1e9, "mfma_tflops": flops / (mean * 1e-3) / 1e12,
+                    "roofline_us": roof * 1e6, "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                    "frac": roof / (mean * 1e-3)}
+        log(f"{key}: {mean:.4f} ms (roofline {roof * 1e6:.1f} us, frac {roof / (mean * 1e-3):.3f})")
+        del ws
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -282,6 +351,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.configs_only:
+        Xh = device_tokens(torch, CF.HEADLINE.N, CF.HEADLINE.h, args.seed, dev)
+        print(json.dumps({"configs": config_legs(args, torch, R, CF, dev, stream, Xh)}), flush=True)
+        return 0
 
     t0 = time.time()
     log(f"generating {cfg.name}: N={cfg.N} h={cfg.h} M={cfg.M} r={cfg.r} k={cfg.k}")
@@ -525,6 +598,8 @@ def main():
         log(f"fullrank {fr_ms:.3f} ms")
         del W, wsw
 
+    if not args.no_configs:
+        result["configs"] = config_legs(args, torch, R, CF, dev, stream, X)
     if not args.no_cpu:
         result["cpu_baseline"], result["parity"] = cpu_leg(args, cfg, gate, X_np, R1_np, R2_np, b_np, ref)
 
