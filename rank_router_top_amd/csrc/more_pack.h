@@ -42,8 +42,10 @@ struct PackArgs {
   float* biasp;       // [NT][2][16] fp32, accumulator layout (fp32 kernels)
   uint32_t* biasq;    // [NT][64] bf16 pairs (hi, lo) as an MFMA A operand (bf16 kernels)
   int* perm;          // [Mpad]: read (with a bias: sorted beforehand) or written (without)
-  float* colnorm2;    // [Mpad] or null: squared norm of the packed column at each sweep position
   int sorted;         // 1: perm was written by order_count_kernel (bias-descending order)
+  int* status;        // the routing calls' stall word: cleared
+  int* seed;          // seed-pass length of the LDS-ring sweep (tiles), written
+  int seed_tiles;
 };
 
 // Element type helpers.
@@ -75,36 +77,23 @@ __global__ __launch_bounds__(1024) void pack_kernel(PackArgs a) {
     // ---- sweep position pos holds expert j = perm[pos] (sorted by
     // order_count_kernel with a bias; index order otherwise); padding last
     const int jl = tid & 63, slice = tid >> 6;   // 64 positions x 16 slices
-    // Mpad is a multiple of 64, so every position of the block is real (no
-    // early exit before the barrier below)
+    // Mpad is a multiple of 64: every position of the block is real
     const int pos = blockIdx.x * 64 + jl;
     const int j = a.sorted ? a.perm[pos] : (pos < a.M ? pos : -1);
     const int t = pos >> 5, i = pos & 31;
     const T* B = (const T*)a.R2;
     T* Bp = (T*)a.R2p;
     // gather column j of R2 (or W) into the packed tile at row i
-    float sq = 0.f;
     for (int w = slice; w < a.ksteps2 * 2 * EPL; w += 16) {
       const int m = w / (2 * EPL), hf = (w / EPL) & 1, e = w % EPL;
       const int kr = k_row<DT>(m, e, hf, a.natural_k);
       T val = 0;
       if (j >= 0 && kr < a.kdim) val = B[(size_t)kr * a.M + j];
       Bp[(((size_t)t * a.ksteps2 + m) * kWave + i + 32 * hf) * EPL + e] = val;
-      float f;
-      if constexpr (DT == 0) f = __uint_as_float((uint32_t)val << 16);
-      else f = (float)val;
-      sq = __builtin_fmaf(f, f, sq);
     }
-    if (a.colnorm2) {
-      // the 16 slices' partial sums of squares -> the column's squared norm
-      __shared__ float part[16][64];
-      part[slice][jl] = sq;
-      __syncthreads();
-      if (slice == 0) {
-        float t2 = 0.f;
-        for (int q = 0; q < 16; ++q) t2 += part[q][jl];
-        a.colnorm2[pos] = t2;
-      }
+    if (blockIdx.x == 0 && tid == 0) {
+      *a.status = 0;
+      *a.seed = a.seed_tiles;
     }
     if (slice == 0) {
       if (!a.sorted) a.perm[pos] = j;

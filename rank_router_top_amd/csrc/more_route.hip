@@ -42,7 +42,7 @@ size_t log_bytes(int kmax) { return (size_t)(2 * kmax + 8) * kWave * sizeof(floa
 
 struct Layout {
   int NT, Mpad, r16, rb, ks1, ks2, ksq, epl, esize;
-  size_t off_status, off_r1p, off_r2p, off_bias, off_biasq, off_perm, off_r1q, off_colnorm, off_bmin, off_wstat, total;
+  size_t off_status, off_r1p, off_r2p, off_bias, off_biasq, off_perm, off_r1q, off_seed, total;
 };
 
 // Workspace layout of one call.  All offsets are 256-byte aligned.
@@ -94,11 +94,8 @@ bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, L
   L->off_r1q = off;
   off += align_up((size_t)L->ksq * L->r16 * 1024);
   // weight statistics of the sweep kernel's error bound and seed pass
-  L->off_colnorm = off;
-  off += align_up((size_t)L->Mpad * sizeof(float));
-  L->off_bmin = off;
-  off += align_up((size_t)L->NT * sizeof(float));
-  L->off_wstat = off;
+  // seed-pass length of the LDS-ring sweep
+  L->off_seed = off;
   off += kAlign;
   L->total = off;
   return true;
@@ -346,8 +343,7 @@ more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int k
   sa.Z = pa.Z;
   sa.R2p = a.R2p;
   sa.biasq = a.biasq;
-  sa.bmin = (const float*)(ws + L.off_bmin);
-  sa.wstat = (const float*)(ws + L.off_wstat);
+  sa.seed = (const int*)(ws + L.off_seed);
   sa.perm = a.perm;
   sa.N = a.N;
   sa.NB = (int)nb;
@@ -413,7 +409,8 @@ more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* 
   p.biasp = (float*)(ws + L.off_bias);
   p.biasq = (uint32_t*)(ws + L.off_biasq);
   p.perm = (int*)(ws + L.off_perm);
-  p.colnorm2 = (float*)(ws + L.off_colnorm);
+  p.status = (int*)(ws + L.off_status);
+  p.seed = (int*)(ws + L.off_seed);
   const bool ordered = bias && M <= kOrderMaxM;
   if (ordered) {
     // sweep order: experts by (bias desc, index asc)
@@ -426,24 +423,12 @@ more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* 
     if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
   }
   p.sorted = ordered ? 1 : 0;
+  p.seed_tiles = ordered ? std::min(L.NT, kPcSeedTiles) : L.NT;
   const int blocks = p.rank_blocks + p.r1_blocks + p.r1q_blocks;
   if (dt == MORE_DT_BF16)
     hipLaunchKernelGGL(pack_kernel<0>, dim3(blocks), dim3(1024), 0, stream, p);
   else
     hipLaunchKernelGGL(pack_kernel<1>, dim3(blocks), dim3(1024), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
-  TileStatArgs ts;
-  ts.bias = bias;
-  ts.perm = p.perm;
-  ts.colnorm2 = p.colnorm2;
-  ts.Mpad = L.Mpad;
-  ts.NT = L.NT;
-  ts.ordered = ordered ? 1 : 0;
-  ts.seed_tiles = std::min(L.NT, kPcSeedTiles);
-  ts.bmin = (float*)(ws + L.off_bmin);
-  ts.wstat = (float*)(ws + L.off_wstat);
-  ts.status = (int*)(ws + L.off_status);
-  hipLaunchKernelGGL(tilestat_kernel, dim3(1), dim3(1024), 0, stream, ts);
   return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 

@@ -20,27 +20,23 @@
 // refilled once every consumer has read it: the ring (RING tiles) absorbs the
 // consumers' different speeds.
 //
-// Exact top-k per token (ties to the lower expert index):
-//   seed pass (the first P tiles of the sweep order -- bias descending, so they
-//     hold most winners -- or every tile without a bias): hi-only logits
-//     z_hi R2 (R16 MFMAs per tile, no bias); per lane and tile the maximum plus
-//     the smallest bias of the tile is at most the logit of one real expert
-//     (up to eps below); each lane keeps the k largest of these (v_med3 list),
-//     and the two lanes of a token merge theirs: thr = k-th largest - eps is a
-//     lower bound of the token's k-th exact logit.  eps bounds |exact - hi-only|
-//     per token: ||z_lo|| max_m ||R2[:, m]|| (the dropped z_lo term,
-//     Cauchy-Schwarz) + 2^-15 (||z_hi|| max_m ||R2[:, m]|| + max |b|), which
-//     covers the fp32 accumulation of either MFMA chain and the bf16 hi + lo
-//     representation of the bias.
-//   main sweep (every tile): exact logits, bias included, from 2 R16 + 1 MFMAs
-//     (z_hi, z_lo, and the bias as a bf16 hi + lo operand against a ones
-//     operand); a 4-logit group whose maximum reaches thr is appended to the
-//     lane's log (16 bytes + a 16-bit sweep position).  Every top-k logit is
-//     >= thr, so it is logged.  When a lane's log is nearly full -- and once
-//     after the first kTightenTile main tiles, where the high-bias winners
-//     are -- the whole wave tightens: thr rises to the token's k-th largest
-//     logged group maximum (each is the exact logit of a distinct expert, so
-//     still a lower bound of the k-th logit) and groups below it are dropped.
+// Exact top-k per token (ties to the lower expert index).  Every tile's
+// logits are exact (bias included): the bias as a bf16 hi + lo operand
+// against a ones operand, then z_hi and z_lo against the tile's R2 operands
+// (2 R16 + 1 MFMAs, fp32 accumulation).
+//   seed pass (the first P tiles of the sweep order -- bias descending, so
+//     they hold most winners -- or every tile without a bias): each lane keeps
+//     the k largest of its tile maxima (v_med3 list); a tile maximum is the
+//     logit of one expert, so the k-th largest over the token's two lanes,
+//     thr, is at most its k-th logit.
+//   main sweep (every tile): a 4-logit group whose maximum reaches thr is
+//     appended to the lane's log (16 bytes + a 16-bit sweep position).  Every
+//     top-k logit is >= thr, so it is logged.  When some lane's appends would
+//     not fit -- and once after the first kTightenTile main tiles, where the
+//     high-bias winners are -- the whole wave tightens: thr rises to the
+//     token's k-th largest logged group maximum (each is the logit of a
+//     distinct expert, so still a lower bound of the k-th logit) and groups
+//     below it are dropped.
 //   finish: the token's k largest logged logits (v_med3 lists merged across
 //     the two lanes) give the k-th value; each lane writes the sweep position
 //     of each of its selected logits at its rank; exact ties fall back to an
@@ -63,8 +59,7 @@ struct SweepArgs {
   const void* Z;             // [NB][hi, lo][R16][64 lanes][16 B]: z of every 32-token block
   const void* R2p;           // [NT][R16][64 lanes][16 B]: A operands, sweep order
   const uint32_t* biasq;     // [NT][64]: (b_hi | b_lo << 16) of row l in lane l < 32, 0 above
-  const float* bmin;         // [NT]: smallest bias of the tile's experts (-inf if it has padding)
-  const float* wstat;        // [3]: max_m ||R2[:, m]||_2, max_m |b_m|, seed tiles P (int bits, 1 <= P <= NT)
+  const int* seed;           // seed tiles P (1 <= P <= NT): written by the packing call
   const int* perm;           // [Mpad]: sweep position -> expert
   long long N;
   int NB, NT, k;              // blocks, tiles, k
@@ -442,7 +437,7 @@ __global__ __launch_bounds__(64 * (NC + kSwLoaders)) void sweep_kernel(SweepArgs
   const int G = gridDim.x, w = blockIdx.x;
   const int NT = a.NT;
   // seed tiles, even (NT is even: the expert count is padded to a multiple of 64)
-  const int P = min((max(__builtin_amdgcn_readfirstlane(__float_as_int(a.wstat[2])), 1) + 1) & ~1, NT);
+  const int P = min((max(__builtin_amdgcn_readfirstlane(*a.seed), 1) + 1) & ~1, NT);
   const int Lseq = P + NT;
   if (threadIdx.x < 64) ((int*)sw_lds)[threadIdx.x] = 0;
   __syncthreads();
