@@ -240,6 +240,34 @@ def test_hypercube_router(oracle_lib):
     compare(o, g, 4, False, 2e-4, "hypercube", at)
 
 
+def test_hypercube_loads_within_bernstein_bound_gpu(oracle_lib):
+    """Prop. 1 / Lemma 4 on the GPU's selection: under the hypercube router each
+    expert is chosen with probability exactly k/M (the sign symmetry survives
+    the bf16 rounding of the Gaussian tokens); over n tokens every load lies
+    within sqrt(2 n k L / M) + 2L/3 of n k / M with probability >= 1 - delta,
+    L = log(2M/delta).  Seeded: one fixed draw that must satisfy the bound; the
+    selection is also held to the oracle's by the parity rule."""
+    r, h, k, n, delta = 8, 64, 4, 1 << 16, 1e-3
+    M = 2 ** r
+    R1 = np.zeros((h, 16), np.float32)
+    R1[:r, :r] = np.eye(r)
+    bits = (np.arange(M)[None, :] >> np.arange(r)[:, None]) & 1
+    R2 = np.zeros((16, M), np.float32)
+    R2[:r] = np.where(bits == 1, 1.0, -1.0)
+    rng = np.random.default_rng(2025)
+    X = I.f32_to_bf16_bits(rng.standard_normal((n, h)).astype(np.float32))
+    R1b, R2b = I.f32_to_bf16_bits(R1), I.f32_to_bf16_bits(R2)
+    say("hypercube loads")
+    g = run_lowrank(X, R1b, R2b, None, k, 0)
+    loads = np.bincount(g["idx"].ravel(), minlength=M)
+    L = math.log(2 * M / delta)
+    bound = math.sqrt(2 * n * k * L / M) + 2 * L / 3
+    assert loads.sum() == n * k
+    assert np.max(np.abs(loads - n * k / M)) <= bound, (np.max(np.abs(loads - n * k / M)), bound)
+    o = oracle_lib.route_lowrank(X, R1b, R2b, None, k, 0)
+    compare(o, g, k, False, 2e-4, "hypercube-loads", oracle_lib.logits_at(X, R1b, R2b, None, g["idx"]))
+
+
 def test_expert_permutation_equivariance():
     """Lemma 3: permuting R2's columns and the bias permutes the indices; gates unchanged."""
     cfg = CF.HEADLINE
