@@ -192,8 +192,9 @@ size_t more_balance_workspace_bytes(more_dtype dt, int64_t N, int64_t h, int64_t
  *   offsets        M + 1 int32: expert e owns positions offsets[e] ..
  *                  offsets[e+1] - 1; offsets[M] = N k.
  *   workspace      at least more_dispatch_workspace_bytes(N, k, M) bytes,
- *                  256-byte aligned (per-block digit counts; for M > 64 one
- *                  extra N k key + slot buffer), overwritten.
+ *                  256-byte aligned (per-block digit counts, about 2 bytes
+ *                  per entry at M >= 4096; for M > 4096 one extra N k key +
+ *                  slot buffer), overwritten.
  * Contract: N k < 2^31 - 1, 1 <= k <= M <= 2^24.  N = 0 is a no-op.  Integer
  * work only: the result is exact and deterministic.
  */
@@ -213,8 +214,9 @@ size_t more_dispatch_workspace_bytes(int64_t N, int32_t k, int64_t M);
  * key + slot buffer of the multi-pass sort) is a static 32 MiB device array
  * of the library, one per GPU, held until the process ends; no call here
  * allocates or frees memory.  A call whose more_dispatch_workspace_bytes(N,
- * k, M) exceeds 32 MiB (N k above about 4.1 million entries for M > 64)
- * returns MORE_ERR_SCRATCH_LIMIT and enqueues nothing.  Every call on one
+ * k, M) exceeds 32 MiB (N k above about 16.7 million entries for M <= 4096,
+ * 3.3 million for M > 4096) returns MORE_ERR_SCRATCH_LIMIT and enqueues
+ * nothing.  Every call on one
  * GPU uses that GPU's one array and leaves it overwritten: calls that may
  * overlap on one GPU (different streams, or threads without ordering) race
  * and must be serialised by the caller.  MORE_ERR_HIP if the array's device

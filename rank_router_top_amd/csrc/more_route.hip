@@ -887,8 +887,7 @@ size_t more_dispatch_workspace_bytes(int64_t N, int32_t k, int64_t M) {
   if (N < 0 || k < 1 || M < 1 || M > (1 << 24) || (int64_t)k > M || N * (int64_t)k >= ((int64_t)1 << 31) - 1)
     return 0;
   const int64_t n = N * k;
-  const int64_t B = (n + kSortBlock - 1) / kSortBlock;
-  size_t bytes = align_up(((size_t)(B > 0 ? B : 1) + 1) * kSortBuckets * sizeof(int));
+  size_t bytes = align_up(sort_hist_ints(n, M) * sizeof(int));
   if (sort_passes(M) > 1) bytes += 2 * align_up((size_t)(n > 0 ? n : 1) * sizeof(int));
   return bytes;
 }
@@ -922,12 +921,11 @@ more_status dispatch_sort_check(const int32_t* topk_idx, int64_t N, int32_t k, i
 more_status dispatch_sort_run(const int32_t* topk_idx, int64_t N, int32_t k, int64_t M, int32_t* sorted_expert,
                               int32_t* sorted_slot, int32_t* offsets, char* ws, hipStream_t stream) {
   const int n = (int)(N * k);
-  const int64_t B = (n + kSortBlock - 1) / kSortBlock;
   int* hist = (int*)ws;
   int* tk = nullptr;
   int* tv = nullptr;
   if (sort_passes(M) > 1) {
-    const size_t off = align_up(((size_t)B + 1) * kSortBuckets * sizeof(int));
+    const size_t off = align_up(sort_hist_ints(n, M) * sizeof(int));
     tk = (int*)(ws + off);
     tv = (int*)(ws + off + align_up((size_t)n * sizeof(int)));
   }

@@ -175,11 +175,13 @@ def test_balance_workspace_bytes():
 
 
 def test_dispatch_workspace_and_validation():
-    """Digit counts (64 per block of 4096 entries, plus 64 row totals, 256-byte
-    aligned) and, for more than one radix pass (M > 64), a key and a slot
-    buffer of N k entries."""
-    assert R.dispatch_workspace_bytes(262144, 8, 4096) == 513 * 64 * 4 + 2 * 262144 * 8 * 4
+    """Digit counts (min(M, 4096) per block of 8192 entries, plus one row of
+    digit totals, 256-byte aligned) and, for more than one pass (M > 4096), a
+    key and a slot buffer of N k entries."""
+    assert R.dispatch_workspace_bytes(262144, 8, 4096) == 257 * 4096 * 4
     assert R.dispatch_workspace_bytes(1000, 4, 64) == 512
+    assert R.dispatch_workspace_bytes(1000, 4, 300) == 2560                       # 2 x 300 ints, aligned
+    assert R.dispatch_workspace_bytes(262144, 8, 4097) == 257 * 4096 * 4 + 2 * 262144 * 8 * 4
     assert R.dispatch_workspace_bytes(1000, 5, 4) == 0          # k > M
     assert R.dispatch_workspace_bytes(1 << 28, 8, 4096) == 0     # N k >= 2^31 - 1
     f = R.lib().more_dispatch_sort
@@ -200,8 +202,10 @@ def test_dispatch_noalloc_rejects_before_any_hip_call():
     assert f(ODD, 10, 4, 64, FAKE, FAKE, FAKE, None) == 9
     assert f(FAKE, 0, 4, 64, None, None, None, None) == 0                   # N = 0: no-op
     assert f(FAKE, -1, 4, 64, FAKE, FAKE, FAKE, None) == 2
-    assert R.dispatch_workspace_bytes(1 << 19, 8, 4096) > 32 << 20
-    assert f(FAKE, 1 << 19, 8, 4096, FAKE, FAKE, FAKE, None) == R.MORE_ERR_SCRATCH_LIMIT
+    assert R.dispatch_workspace_bytes(1 << 19, 8, 65536) > 32 << 20
+    assert f(FAKE, 1 << 19, 8, 65536, FAKE, FAKE, FAKE, None) == R.MORE_ERR_SCRATCH_LIMIT
+    assert R.dispatch_workspace_bytes(1 << 22, 8, 4096) > 32 << 20
+    assert f(FAKE, 1 << 22, 8, 4096, FAKE, FAKE, FAKE, None) == R.MORE_ERR_SCRATCH_LIMIT
     assert R.status_str(R.MORE_ERR_SCRATCH_LIMIT) != "unknown status"
 
 

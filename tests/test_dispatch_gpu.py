@@ -44,14 +44,16 @@ def check(oracle_lib, idx, M, label):
 
 @pytest.mark.parametrize("N,M,k", [
     (1, 4096, 8),          # a single token
-    (1000, 4096, 8),       # two radix passes, one block
-    (4096 // 8 + 3, 4096, 8),   # just over one block of 4096 entries
-    (5000, 64, 4),         # one pass (6-bit experts)
-    (5000, 65, 4),         # two passes, the second with one live bit
+    (1000, 4096, 8),       # one pass, one block
+    (8192 // 8 + 3, 4096, 8),   # just over one block of 8192 entries
+    (5000, 64, 4),         # one pass, few experts: repeated digits in every round
+    (5000, 65, 4),         # one pass, M not a power of two
+    (5000, 4097, 4),       # two passes, the second with one live bit
     (3000, 1, 1),          # a single expert
-    (20000, 65536, 16),    # three passes
-    (777, 1 << 24, 3),     # four passes, the largest M
+    (20000, 65536, 16),    # two passes, 40 blocks (blocks spread over the XCDs)
+    (777, 1 << 24, 3),     # two full 12-bit passes, the largest M
     (4096 + 1, 300, 7),    # ragged
+    (16384, 4096, 4),      # 8 blocks: one per XCD
 ])
 def test_dispatch_shapes(oracle_lib, N, M, k):
     idx = I.make_expert_sets(2, 61, N, M, k)
