@@ -43,8 +43,8 @@ struct PackArgs {
   uint32_t* biasq;    // [NT][64] bf16 pairs (hi, lo) as an MFMA A operand (bf16 kernels)
   int* perm;          // [Mpad]: read (with a bias: sorted beforehand) or written (without)
   int sorted;         // 1: perm was written by order_count_kernel (bias-descending order)
-  int* status;        // the routing calls' stall word: cleared
-  int* seed;          // seed-pass length of the LDS-ring sweep (tiles), written
+  int* status;        // the routing calls' stall word: cleared (null: left alone)
+  int* seed;          // seed-pass length of the LDS-ring sweep (tiles), written (null: left alone)
   int seed_tiles;
 };
 
@@ -73,6 +73,10 @@ __global__ __launch_bounds__(1024) void pack_kernel(PackArgs a) {
   typedef typename Elem<DT>::T T;
   constexpr int EPL = (DT == 0) ? 8 : 1;          // elements per lane per K-step
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0) {
+    if (a.status) *a.status = 0;
+    if (a.seed) *a.seed = a.seed_tiles;
+  }
   if ((int)blockIdx.x < a.rank_blocks) {
     // ---- sweep position pos holds expert j = perm[pos] (sorted by
     // order_count_kernel with a bias; index order otherwise); padding last
@@ -90,10 +94,6 @@ __global__ __launch_bounds__(1024) void pack_kernel(PackArgs a) {
       T val = 0;
       if (j >= 0 && kr < a.kdim) val = B[(size_t)kr * a.M + j];
       Bp[(((size_t)t * a.ksteps2 + m) * kWave + i + 32 * hf) * EPL + e] = val;
-    }
-    if (blockIdx.x == 0 && tid == 0) {
-      *a.status = 0;
-      *a.seed = a.seed_tiles;
     }
     if (slice == 0) {
       if (!a.sorted) a.perm[pos] = j;

@@ -291,8 +291,10 @@ more_status launch_splitm(const LowRankArgs& a, const Layout& L, const SplitmPla
   return launch_topk_merge(m, full, stream) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 
+// join: if set, the stream waits for it after the projection (the packed
+// sweep operands come from a side stream that overlapped the projection).
 more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int kmax, bool full, bool lse_mode,
-                         bool ring, char* ws, hipStream_t stream) {
+                         bool ring, char* ws, hipStream_t stream, hipEvent_t join = nullptr) {
   int ksp = 0;
   bool tail = false;
   proj_ksteps(h, L.r16, &ksp, &tail);
@@ -319,6 +321,7 @@ more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int k
   const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (2 * nb + kProjWaves - 1) / kProjWaves));
   hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, stream, pa);
   if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
+  if (join && hipStreamWaitEvent(stream, join, 0) != hipSuccess) return MORE_ERR_HIP;
   if (!ring) {
     // every wave reads the R2 tiles from memory itself
     const size_t rt_lds = route_lds_bytes(kmax, L.Mpad);
@@ -379,9 +382,15 @@ lowrank_fn pick_lowrank(more_dtype dt, bool full, int kmax, int r16) {
   return pick_lowrank_f32(full, kmax, r16);
 }
 
+// What one launch_pack call enqueues: everything, or the two halves of the
+// whole routing call's split (the projection's R1 operands and the stall
+// word on the caller's stream; the sweep order, R2, bias and R1 of the other
+// kernels on a side stream, overlapping the projection).
+enum PackPart { kPackAll, kPackProjection, kPackSweep };
+
 more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* B, const float* bias,
                         int64_t h, int64_t r, int64_t M, const Layout& L, char* ws,
-                        hipStream_t stream) {
+                        hipStream_t stream, PackPart part = kPackAll) {
   PackArgs p;
   memset(&p, 0, sizeof p);
   p.R1 = fullrank ? nullptr : A;
@@ -411,8 +420,16 @@ more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* 
   p.perm = (int*)(ws + L.off_perm);
   p.status = (int*)(ws + L.off_status);
   p.seed = (int*)(ws + L.off_seed);
+  if (part == kPackProjection) {
+    p.rank_blocks = 0;
+    p.r1_blocks = 0;
+    p.seed = nullptr;
+  } else if (part == kPackSweep) {
+    p.r1q_blocks = 0;
+    p.status = nullptr;
+  }
   const bool ordered = bias && M <= kOrderMaxM;
-  if (ordered) {
+  if (ordered && part != kPackProjection) {
     // sweep order: experts by (bias desc, index asc)
     OrderArgs o;
     o.bias = bias;
@@ -424,7 +441,7 @@ more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* 
   }
   p.sorted = ordered ? 1 : 0;
   p.seed_tiles = ordered ? std::min(L.NT, kPcSeedTiles) : L.NT;
-  const int blocks = p.rank_blocks + p.r1_blocks + p.r1q_blocks;
+  const int blocks = std::max(1, p.rank_blocks + p.r1_blocks + p.r1q_blocks);
   if (dt == MORE_DT_BF16)
     hipLaunchKernelGGL(pack_kernel<0>, dim3(blocks), dim3(1024), 0, stream, p);
   else
@@ -506,10 +523,16 @@ more_status more_lowrank_pack(more_dtype dt, const void* R1, int64_t h, int64_t 
   return launch_pack(dt, 0, R1, R2, bias, h, r, M, L, (char*)workspace, (hipStream_t)stream);
 }
 
-more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int64_t r,
-                                      int64_t M, int32_t k, more_gate gate, int32_t* topk_idx,
-                                      float* topk_gate, float* topk_logit, float* lse,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The routing call on packed weights.  join: the packed sweep operands are
+// still being written on a side stream and this event marks their end; every
+// path waits for it before its first kernel that reads them.
+more_status route_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k,
+                         more_gate gate, int32_t* topk_idx, float* topk_gate, float* topk_logit, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream, hipEvent_t join) {
   // R1/R2 are not read here; a non-null placeholder keeps the shared validation.
   more_status st = validate(0, dt, X, N, h, X, r, X, M, nullptr, k, gate, topk_idx, topk_gate,
                             topk_logit, lse);
@@ -539,16 +562,18 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   a.out_lse = full ? lse : nullptr;
   const size_t shmem = (size_t)waves * log_bytes(kmax);
   SplitmPlan sp;
-  if (path_allowed(kPathSplitM) && splitm_plan(dt, L, N, h, k, &sp) && workspace_bytes >= L.total + sp.bytes &&
-      4 * log_bytes(kmax) <= (size_t)kLdsBytes)
-    return launch_splitm(a, L, sp, kmax, full, ws + L.total, (hipStream_t)stream);
   const size_t zbytes = z_scratch_bytes(dt, L, N);
-  if (zbytes > 0 && workspace_bytes >= L.total + zbytes) {
+  const bool splitm = path_allowed(kPathSplitM) && splitm_plan(dt, L, N, h, k, &sp) &&
+                      workspace_bytes >= L.total + sp.bytes && 4 * log_bytes(kmax) <= (size_t)kLdsBytes;
+  if (!splitm && zbytes > 0 && workspace_bytes >= L.total + zbytes) {
     if (path_allowed(kPathSplit) && split_fits(kmax, L, h, false))
-      return launch_split(a, L, h, kmax, full, full, false, ws, (hipStream_t)stream);
+      return launch_split(a, L, h, kmax, full, full, false, ws, (hipStream_t)stream, join);
     if (path_allowed(kPathRing) && split_fits(kmax, L, h, true))
-      return launch_split(a, L, h, kmax, full, full, true, ws, (hipStream_t)stream);
+      return launch_split(a, L, h, kmax, full, full, true, ws, (hipStream_t)stream, join);
   }
+  // every other path reads packed sweep operands in its first kernel
+  if (join && hipStreamWaitEvent((hipStream_t)stream, join, 0) != hipSuccess) return MORE_ERR_HIP;
+  if (splitm) return launch_splitm(a, L, sp, kmax, full, ws + L.total, (hipStream_t)stream);
   const size_t pc_lds = (dt == MORE_DT_BF16 && L.ksq > 0) ? pc_lds_bytes(kmax, L.r16, L.Mpad) : 0;
   if (pc_lds > 0 && (long long)pc_lds <= kLdsBytes && path_allowed(kPathPc)) {
     // Producer/consumer kernel: one 12-wave workgroup per CU, persistent.
@@ -629,6 +654,47 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
   return hipGetLastError() == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 
+// Side stream (default priority, no implicit synchronisation with the null
+// stream) and fork/join events of the whole routing call, one set per
+// device, created on first use.  g_side_mu is held from the fork to the
+// caller stream's wait on the join, so the events are never re-recorded by
+// another call in between.
+constexpr int kSideDevices = 64;
+std::mutex g_side_mu;
+hipStream_t g_side_stream[kSideDevices] = {};
+hipEvent_t g_side_fork[kSideDevices] = {};
+hipEvent_t g_side_join[kSideDevices] = {};
+
+bool side_stream(int dev) {
+  if (dev < 0 || dev >= kSideDevices) return false;
+  if (g_side_stream[dev]) return true;
+  hipStream_t s = nullptr;
+  hipEvent_t f = nullptr, j = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return false;
+  if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+    if (f) (void)hipEventDestroy(f);
+    (void)hipStreamDestroy(s);
+    return false;
+  }
+  g_side_stream[dev] = s;
+  g_side_fork[dev] = f;
+  g_side_join[dev] = j;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int64_t r,
+                                      int64_t M, int32_t k, more_gate gate, int32_t* topk_idx,
+                                      float* topk_gate, float* topk_logit, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return route_packed(dt, X, N, h, r, M, k, gate, topk_idx, topk_gate, topk_logit, lse, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
 more_status more_route_lowrank(more_dtype dt, const void* X, int64_t N, int64_t h, const void* R1,
                                int64_t r, const void* R2, int64_t M, const float* bias, int32_t k,
                                more_gate gate, int32_t* topk_idx, float* topk_gate,
@@ -637,10 +703,39 @@ more_status more_route_lowrank(more_dtype dt, const void* X, int64_t N, int64_t 
   more_status st = validate(0, dt, X, N, h, R1, r, R2, M, bias, k, gate, topk_idx, topk_gate,
                             topk_logit, lse);
   if (st != MORE_OK || N == 0) return st;
-  st = more_lowrank_pack(dt, R1, h, r, R2, M, bias, workspace, workspace_bytes, stream);
+  Layout L;
+  make_layout(0, dt, h, r, M, &L);
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace % kAlign) != 0)
+    return MORE_ERR_WORKSPACE;
+  const hipStream_t hs = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int dev = -1;
+  // bf16 with a bias: the sweep order and the sweep operands are packed on a
+  // side stream while the projection (which needs only its own R1 operands)
+  // runs on the caller's stream
+  if (dt == MORE_DT_BF16 && bias && M <= kOrderMaxM && L.ksq > 0 && hipGetDevice(&dev) == hipSuccess) {
+    std::lock_guard<std::mutex> guard(g_side_mu);
+    if (side_stream(dev)) {
+      const hipStream_t side = g_side_stream[dev];
+      if (hipEventRecord(g_side_fork[dev], hs) != hipSuccess ||
+          hipStreamWaitEvent(side, g_side_fork[dev], 0) != hipSuccess)
+        return MORE_ERR_HIP;
+      st = launch_pack(dt, 0, R1, R2, bias, h, r, M, L, ws, side, kPackSweep);
+      if (st != MORE_OK) return st;
+      if (hipEventRecord(g_side_join[dev], side) != hipSuccess) return MORE_ERR_HIP;
+      st = launch_pack(dt, 0, R1, R2, bias, h, r, M, L, ws, hs, kPackProjection);
+      if (st == MORE_OK)
+        st = route_packed(dt, X, N, h, r, M, k, gate, topk_idx, topk_gate, topk_logit, lse, workspace,
+                          workspace_bytes, stream, g_side_join[dev]);
+      // on an error the caller's stream still joins the side stream's work
+      if (st != MORE_OK) (void)hipStreamWaitEvent(hs, g_side_join[dev], 0);
+      return st;
+    }
+  }
+  st = launch_pack(dt, 0, R1, R2, bias, h, r, M, L, ws, hs);
   if (st != MORE_OK) return st;
-  return more_lowrank_route_packed(dt, X, N, h, r, M, k, gate, topk_idx, topk_gate, topk_logit, lse,
-                                   workspace, workspace_bytes, stream);
+  return route_packed(dt, X, N, h, r, M, k, gate, topk_idx, topk_gate, topk_logit, lse, workspace,
+                      workspace_bytes, stream, nullptr);
 }
 
 size_t more_balance_workspace_bytes(more_dtype dt, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k) {
