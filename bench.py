@@ -527,7 +527,7 @@ def main():
         log(f"dispatch call mean {d_mean:.4f} ms (p10 {d_p10:.4f}, p90 {d_p90:.4f})")
         result["dispatch"] = {
             "entry": "more_dispatch_sort", "ms_per_call": d_mean, "ms_median": d_med, "ms_p10": d_p10,
-            "ms_p90": d_p90, "entries": nk, "radix_passes": 2 if cfg.M > 64 else 1,
+            "ms_p90": d_p90, "entries": nk, "digit_passes": 1 if cfg.M <= 4096 else -(-(cfg.M - 1).bit_length() // 12),
             "roofline": {"bound": "hbm", "achieved": d_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": d_ach / HBM_PEAK_GBS, "algorithmic_bytes_per_call": d_bytes}}
         del dws, dout

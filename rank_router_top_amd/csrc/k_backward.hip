@@ -203,15 +203,18 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
   constexpr int NTH = 64 * kBwdExpWaves;
   constexpr int ZB = 2 * R16 * 1024;              // z block bytes
   constexpr int SELMAX = 64 * NS;                 // >= 32 k entries (NS = ceil(32 k / 64))
+  constexpr int ZRS = kBwdRow + 4;
+  constexpr int DTS = kTile + 4;                  // padded expert-column row of the tvbar tile
+  constexpr int DTT = kTile * DTS;                // floats of one tile
   struct Buf {
     u32x4 z[ZB / 16];
     float lse[kTile], g[kTile];
-    float zr[kTile * kBwdRow];
+    float zr[kTile * ZRS];   // z rows, padded to ZRS floats (the hf halves read other banks)
     int sp[SELMAX];
     float sv[SELMAX];
   };
   __shared__ __align__(16) Buf buf[2];
-  __shared__ __align__(16) float dt[kBwdExpWaves][TW * kTile * kTile];   // per wave: tvbar of its tiles [tile][expert col][token]
+  __shared__ __align__(16) float dt[kBwdExpWaves][TW * DTT];   // per wave: tvbar of its tiles [tile][expert col][token]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
       const int c = tid + NTH * i;
       if (c < ZRC) {
         const bool ok = n0 + c / (kBwdRow / 4) < a.N;
-        *(float4*)(B.zr + 4 * c) = ok ? P.zr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        *(float4*)(B.zr + (c / (kBwdRow / 4)) * ZRS + 4 * (c % (kBwdRow / 4))) = ok ? P.zr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
     if (tid < kTile) {
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
     for (int m = 0; m < 2; ++m) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = B.zr[(16 * m + 8 * (e >> 2) + 4 * hf + (e & 3)) * kBwdRow + col];
+      for (int e = 0; e < 8; ++e) x[e] = B.zr[(16 * m + 8 * (e >> 2) + 4 * hf + (e & 3)) * ZRS + col];
       split8(x, zth[m], ztl[m]);
     }
     int spos[NS];
@@ -386,16 +389,16 @@ __global__ __launch_bounds__(64 * kBwdExpWaves) void bwd_exp_kernel(BwdArgs a) {
     // the block's tvbar in the wave's tiles, dense in LDS: cleared, scattered
     // (a token selects an expert at most once), then read like ybar itself
 #pragma unroll
-    for (int i = 0; i < TW * kTile * kTile / 4 / 64; ++i)
+    for (int i = 0; i < TW * DTT / 4 / 64; ++i)
       *(float4*)(my + 4 * (lane + 64 * i)) = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int tl = (spos[i] >> 10) - t0;
-      if (spos[i] >= 0 && tl >= 0 && tl < TW) my[tl * kTile * kTile + (spos[i] & 1023)] = B.sv[lane + 64 * i];
+      if (spos[i] >= 0 && tl >= 0 && tl < TW) my[tl * DTT + ((spos[i] >> 5) & 31) * DTS + (spos[i] & 31)] = B.sv[lane + 64 * i];
     }
 #pragma unroll
     for (int u = 0; u < TW; ++u) {
-      const float* row = my + u * kTile * kTile + col * kTile + 4 * hf;
+      const float* row = my + u * DTT + col * DTS + 4 * hf;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 x = *(const float4*)(row + 8 * q);
@@ -467,8 +470,12 @@ __global__ __launch_bounds__(64 * kBwdXWaves) void bwd_x_kernel(BwdArgs a) {
   constexpr int HT = kBwdXTiles;
   constexpr int WC = HT * kTile;                 // columns of one wave
   constexpr int NCH = kTile * WC / 8 / 64;       // 16-byte chunks of a block slice per lane
-  __shared__ __align__(16) uint16_t xs_all[kBwdXWaves][WC * kTile];   // X^T [column][token]
-  __shared__ __align__(16) uint16_t ys_all[kBwdXWaves][kTile * WC];   // xbar [token][column]
+  // padded rows: a column of X^T is 32 tokens + 8 (80 bytes), so the 16-byte
+  // reads of 16 consecutive columns and the transposed 2-byte writes spread
+  // over the banks; a token row of xbar is WC columns + 8 (16-byte aligned)
+  constexpr int XS = kTile + 8, YS = WC + 8;
+  __shared__ __align__(16) uint16_t xs_all[kBwdXWaves][WC * XS];   // X^T [column][token]
+  __shared__ __align__(16) uint16_t ys_all[kBwdXWaves][kTile * YS];   // xbar [token][column]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int s = blockIdx.x / a.GX, gq = blockIdx.x % a.GX;
@@ -537,7 +544,7 @@ __global__ __launch_bounds__(64 * kBwdXWaves) void bwd_x_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t w32 = v[e >> 1];
-        xs[(cc + e) * kTile + tok] = ok ? (uint16_t)((e & 1) ? (w32 >> 16) : (w32 & 0xffff)) : (uint16_t)0;
+        xs[(cc + e) * XS + tok] = ok ? (uint16_t)((e & 1) ? (w32 >> 16) : (w32 & 0xffff)) : (uint16_t)0;
       }
     }
     const bool tok_ok = n0 + col < a.N;
@@ -574,12 +581,12 @@ __global__ __launch_bounds__(64 * kBwdXWaves) void bwd_x_kernel(BwdArgs a) {
       for (int q = 0; q < 4; ++q) {
         const uint32_t lo = (uint32_t)bf16_bits(xa[4 * q]) | ((uint32_t)bf16_bits(xa[4 * q + 1]) << 16);
         const uint32_t hi = (uint32_t)bf16_bits(xa[4 * q + 2]) | ((uint32_t)bf16_bits(xa[4 * q + 3]) << 16);
-        *(uint2*)(ys + col * WC + u * kTile + 8 * q + 4 * hf) = make_uint2(lo, hi);
+        *(uint2*)(ys + col * YS + u * kTile + 8 * q + 4 * hf) = make_uint2(lo, hi);
       }
       // R1bar^T partial: rows = ranks, column = h; K = the block's tokens
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const bf16x8 xb = __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + (u * kTile + col) * kTile + 16 * m + 8 * hf));
+        const bf16x8 xb = __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + (u * kTile + col) * XS + 16 * m + 8 * hf));
         r1acc[u] = mfma_bf16(zth[m], xb, r1acc[u]);
         r1acc[u] = mfma_bf16(ztl[m], xb, r1acc[u]);
       }
@@ -590,7 +597,7 @@ __global__ __launch_bounds__(64 * kBwdXWaves) void bwd_x_kernel(BwdArgs a) {
       const int q = lane + 64 * i;
       const int tok = q / (WC / 8);
       const int cc = (q % (WC / 8)) * 8;
-      const u32x4 v = *(const u32x4*)(ys + tok * WC + cc);
+      const u32x4 v = *(const u32x4*)(ys + tok * YS + cc);
       if (n0 + tok < a.N && cc < ncol) *(u32x4*)(a.xbar + (n0 + tok) * a.h + c0 + cc) = v;
     }
   };
