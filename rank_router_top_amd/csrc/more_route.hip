@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <mutex>
 
 #include "more_route.h"
@@ -291,10 +292,23 @@ more_status launch_splitm(const LowRankArgs& a, const Layout& L, const SplitmPla
   return launch_topk_merge(m, full, stream) == hipSuccess ? MORE_OK : MORE_ERR_HIP;
 }
 
-// join: if set, the stream waits for it after the projection (the packed
-// sweep operands come from a side stream that overlapped the projection).
+// The side stream's operands-ready word (64 bits): in the stall word's
+// 256-byte block, on its own 128-byte line.
+constexpr size_t kReadyOffset = 128;
+
+// Side-stream packing (the whole routing call): with join, the packed sweep
+// operands come from a side stream that overlapped the projection, and the
+// stream waits for join after the projection.  With token instead, the side
+// stream stores token in the workspace's ready word when they are complete
+// and the routing kernel waits for that word itself, so no cross-stream wait
+// stands between the two kernels.
+struct SideSync {
+  hipEvent_t join = nullptr;
+  unsigned long long token = 0;   // 0: none
+};
+
 more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int kmax, bool full, bool lse_mode,
-                         bool ring, char* ws, hipStream_t stream, hipEvent_t join = nullptr) {
+                         bool ring, char* ws, hipStream_t stream, SideSync side = SideSync()) {
   int ksp = 0;
   bool tail = false;
   proj_ksteps(h, L.r16, &ksp, &tail);
@@ -321,7 +335,8 @@ more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int k
   const int64_t pg = std::max<int64_t>(1, std::min<int64_t>(cus, (2 * nb + kProjWaves - 1) / kProjWaves));
   hipLaunchKernelGGL(pf, dim3((unsigned)pg), dim3(64 * (kProjWaves + 1)), pj_lds, stream, pa);
   if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
-  if (join && hipStreamWaitEvent(stream, join, 0) != hipSuccess) return MORE_ERR_HIP;
+  if (side.join && (ring || !side.token) && hipStreamWaitEvent(stream, side.join, 0) != hipSuccess)
+    return MORE_ERR_HIP;
   if (!ring) {
     // every wave reads the R2 tiles from memory itself
     const size_t rt_lds = route_lds_bytes(kmax, L.Mpad);
@@ -330,6 +345,10 @@ more_status launch_split(const LowRankArgs& a, const Layout& L, int64_t h, int k
       return MORE_ERR_HIP;
     RouteArgs ra;
     ra.base = a;
+    ra.ready = side.token ? (const unsigned long long*)(ws + L.off_status + kReadyOffset) : nullptr;
+    ra.token = side.token;
+    ra.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    ra.status = (int*)(ws + L.off_status);
     ra.base.out_lse = lse_mode ? a.out_lse : nullptr;
     ra.Z = pa.Z;
     ra.NB = (int)nb;
@@ -381,6 +400,19 @@ lowrank_fn pick_lowrank(more_dtype dt, bool full, int kmax, int r16) {
   if (dt == MORE_DT_BF16) return full ? pick_lowrank_bf16_full(kmax, r16) : pick_lowrank_bf16_topk(kmax, r16);
   return pick_lowrank_f32(full, kmax, r16);
 }
+
+}  // namespace
+
+namespace more {
+// Stores the call's token in the operands-ready word after the packing
+// kernels of a side stream (the kernel boundary has made their writes
+// visible at device scope).
+__global__ __launch_bounds__(64) void ready_kernel(unsigned long long* ready, unsigned long long token) {
+  if (threadIdx.x == 0) __hip_atomic_store(ready, token, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+}  // namespace more
+
+namespace {
 
 // What one launch_pack call enqueues: everything, or the two halves of the
 // whole routing call's split (the projection's R1 operands and the stall
@@ -532,7 +564,7 @@ namespace {
 // path waits for it before its first kernel that reads them.
 more_status route_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k,
                          more_gate gate, int32_t* topk_idx, float* topk_gate, float* topk_logit, float* lse,
-                         void* workspace, size_t workspace_bytes, void* stream, hipEvent_t join) {
+                         void* workspace, size_t workspace_bytes, void* stream, SideSync side = SideSync()) {
   // R1/R2 are not read here; a non-null placeholder keeps the shared validation.
   more_status st = validate(0, dt, X, N, h, X, r, X, M, nullptr, k, gate, topk_idx, topk_gate,
                             topk_logit, lse);
@@ -567,12 +599,12 @@ more_status route_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int
                       workspace_bytes >= L.total + sp.bytes && 4 * log_bytes(kmax) <= (size_t)kLdsBytes;
   if (!splitm && zbytes > 0 && workspace_bytes >= L.total + zbytes) {
     if (path_allowed(kPathSplit) && split_fits(kmax, L, h, false))
-      return launch_split(a, L, h, kmax, full, full, false, ws, (hipStream_t)stream, join);
+      return launch_split(a, L, h, kmax, full, full, false, ws, (hipStream_t)stream, side);
     if (path_allowed(kPathRing) && split_fits(kmax, L, h, true))
-      return launch_split(a, L, h, kmax, full, full, true, ws, (hipStream_t)stream, join);
+      return launch_split(a, L, h, kmax, full, full, true, ws, (hipStream_t)stream, side);
   }
   // every other path reads packed sweep operands in its first kernel
-  if (join && hipStreamWaitEvent((hipStream_t)stream, join, 0) != hipSuccess) return MORE_ERR_HIP;
+  if (side.join && hipStreamWaitEvent((hipStream_t)stream, side.join, 0) != hipSuccess) return MORE_ERR_HIP;
   if (splitm) return launch_splitm(a, L, sp, kmax, full, ws + L.total, (hipStream_t)stream);
   const size_t pc_lds = (dt == MORE_DT_BF16 && L.ksq > 0) ? pc_lds_bytes(kmax, L.r16, L.Mpad) : 0;
   if (pc_lds > 0 && (long long)pc_lds <= kLdsBytes && path_allowed(kPathPc)) {
@@ -665,6 +697,16 @@ hipStream_t g_side_stream[kSideDevices] = {};
 hipEvent_t g_side_fork[kSideDevices] = {};
 hipEvent_t g_side_join[kSideDevices] = {};
 
+// Tokens of the ready word: unique per call in this process, counted from a
+// clock-derived base, so a stale word (an earlier call's token, or whatever
+// the caller's memory held) does not hold the current one.
+unsigned long long next_token() {
+  static std::atomic<unsigned long long> next{
+      ((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull) | 1ull};
+  const unsigned long long t = next.fetch_add(1, std::memory_order_relaxed);
+  return t ? t : next.fetch_add(1, std::memory_order_relaxed);
+}
+
 bool side_stream(int dev) {
   if (dev < 0 || dev >= kSideDevices) return false;
   if (g_side_stream[dev]) return true;
@@ -692,7 +734,7 @@ more_status more_lowrank_route_packed(more_dtype dt, const void* X, int64_t N, i
                                       float* topk_gate, float* topk_logit, float* lse,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return route_packed(dt, X, N, h, r, M, k, gate, topk_idx, topk_gate, topk_logit, lse, workspace,
-                      workspace_bytes, stream, nullptr);
+                      workspace_bytes, stream);
 }
 
 more_status more_route_lowrank(more_dtype dt, const void* X, int64_t N, int64_t h, const void* R1,
@@ -717,25 +759,39 @@ more_status more_route_lowrank(more_dtype dt, const void* X, int64_t N, int64_t 
     std::lock_guard<std::mutex> guard(g_side_mu);
     if (side_stream(dev)) {
       const hipStream_t side = g_side_stream[dev];
+      // Under graph capture the call's token would be replayed unchanged, so
+      // there the caller's stream waits for the side stream's event instead.
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(hs, &cap) != hipSuccess) return MORE_ERR_HIP;
+      SideSync sync;
+      sync.join = g_side_join[dev];
+      if (cap == hipStreamCaptureStatusNone) sync.token = next_token();
       if (hipEventRecord(g_side_fork[dev], hs) != hipSuccess ||
           hipStreamWaitEvent(side, g_side_fork[dev], 0) != hipSuccess)
         return MORE_ERR_HIP;
       st = launch_pack(dt, 0, R1, R2, bias, h, r, M, L, ws, side, kPackSweep);
-      if (st != MORE_OK) return st;
+      if (st == MORE_OK && sync.token) {
+        hipLaunchKernelGGL(ready_kernel, dim3(1), dim3(64), 0, side,
+                           (unsigned long long*)(ws + L.off_status + kReadyOffset), sync.token);
+        if (hipGetLastError() != hipSuccess) st = MORE_ERR_HIP;
+      }
       if (hipEventRecord(g_side_join[dev], side) != hipSuccess) return MORE_ERR_HIP;
-      st = launch_pack(dt, 0, R1, R2, bias, h, r, M, L, ws, hs, kPackProjection);
+      if (st == MORE_OK) st = launch_pack(dt, 0, R1, R2, bias, h, r, M, L, ws, hs, kPackProjection);
       if (st == MORE_OK)
         st = route_packed(dt, X, N, h, r, M, k, gate, topk_idx, topk_gate, topk_logit, lse, workspace,
-                          workspace_bytes, stream, g_side_join[dev]);
-      // on an error the caller's stream still joins the side stream's work
-      if (st != MORE_OK) (void)hipStreamWaitEvent(hs, g_side_join[dev], 0);
+                          workspace_bytes, stream, sync);
+      // With a token the routing kernel waited for the side stream's results,
+      // so the caller's stream needs no wait; under capture and on an error it
+      // still joins the side stream (a capture must rejoin every stream it
+      // forked).
+      if (st != MORE_OK || !sync.token) (void)hipStreamWaitEvent(hs, g_side_join[dev], 0);
       return st;
     }
   }
   st = launch_pack(dt, 0, R1, R2, bias, h, r, M, L, ws, hs);
   if (st != MORE_OK) return st;
   return route_packed(dt, X, N, h, r, M, k, gate, topk_idx, topk_gate, topk_logit, lse, workspace,
-                      workspace_bytes, stream, nullptr);
+                      workspace_bytes, stream);
 }
 
 size_t more_balance_workspace_bytes(more_dtype dt, int64_t N, int64_t h, int64_t r, int64_t M, int32_t k) {

@@ -271,6 +271,14 @@ struct RouteArgs {
   const void* Z;      // as written by proj_kernel
   int NB;             // 32-token blocks
   int pre;            // seed-pass tiles with a bias: a multiple of 4 in [4, NT]
+  // non-null: the packed sweep operands come from another stream, which
+  // stores `token` (unique to the call) in *ready when they are complete;
+  // every workgroup waits for it first (bounded: past spin_limit polls it
+  // sets *status and exits)
+  const unsigned long long* ready;
+  unsigned long long token;
+  int spin_limit;
+  int* status;
 };
 
 template <int KMAX>
@@ -296,6 +304,28 @@ __global__ __launch_bounds__(64 * WAVES) void route_kernel(RouteArgs ra) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NT = a.NT;
   const int mpad = NT * kTile;
+  if (ra.ready) {
+    lds_i32* word = (lds_i32*)(rt_lds + L::flag_off(WAVES, mpad));
+    if (threadIdx.x == 0) {
+      // relaxed polls, then one acquire fence (the polls do not invalidate
+      // the caches the other workgroups are already filling)
+      int ok = 1;
+      for (int n = 0; __hip_atomic_load(ra.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ra.token;) {
+        if (++n > ra.spin_limit) {
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (!ok && ra.status) __hip_atomic_store(ra.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *word = ok;
+    }
+    __syncthreads();
+    const int ok = *word;
+    __syncthreads();   // the word is used again below
+    if (!ok) return;   // workgroup-uniform
+  }
   // stage the bias (accumulator layout, -inf on padding rows) and the sweep
   // order (position -> expert, 16 bits: M <= 65535 here)
   bool nz = false;   // any nonzero bias

@@ -70,3 +70,30 @@ def test_tiny_spin_limit_reports_stall(oracle_lib, spin_limit, route_paths, path
     o = oracle_lib.route_lowrank(Xn, R1, R2, b, cfg.k, 0)
     at = oracle_lib.logits_at(Xn, R1, R2, b, g["idx"])
     say(f"ok {compare(o, g, cfg.k, False, 2e-4, 'after-stall', at)}")
+
+
+def test_whole_call_tiny_spin_limit_reports_stall(oracle_lib, spin_limit):
+    """The whole routing call (more_route_lowrank): the sweep operands are
+    packed on a side stream and the routing kernel waits for their ready word
+    with a bounded wait.  With a tiny spin limit the call's waits give up and
+    the stall word says so; with the default limit the call is exact."""
+    cfg = CF.HEADLINE
+    n = 32 * 1024 + 7
+    Xn = cfg.x_rows(0, 0, n, n_total=cfg.N)
+    R1, R2, b = cfg.weights(0)
+    X = R.to_device(Xn, DEV)
+    d = [R.to_device(a, DEV) for a in (R1, R2, b)]
+    nbytes = R.workspace_bytes(False, R.MORE_DT_BF16, n, cfg.h, cfg.r, cfg.M, cfg.k, 0, True)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    say(f"whole call, tiny spin limit: N={n}")
+    spin_limit(1)
+    R.route_lowrank(X, *d, cfg.k, 0, workspace=ws)
+    assert R.route_status(ws) == R.MORE_ERR_STALLED
+    say("whole call, default spin limit")
+    spin_limit(0)
+    g = R.route_lowrank(X, *d, cfg.k, 0, workspace=ws)
+    assert R.route_status(ws) == R.MORE_OK
+    g = {key: (None if v is None else v.cpu().numpy()) for key, v in g.items()}
+    o = oracle_lib.route_lowrank(Xn, R1, R2, b, cfg.k, 0)
+    at = oracle_lib.logits_at(Xn, R1, R2, b, g["idx"])
+    say(f"ok {compare(o, g, cfg.k, False, 2e-4, 'whole-call', at)}")
