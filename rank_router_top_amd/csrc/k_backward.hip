@@ -484,7 +484,12 @@ __global__ __launch_bounds__(64 * kBwdXWaves) void bwd_x_kernel(BwdArgs a) {
   if (ht0 >= nht) return;
   const int c0 = ht0 * kTile;
   const int ncol = (nht - ht0 < HT ? nht - ht0 : HT) * kTile;
-  uint16_t* xs = xs_all[wave];
+  uint32_t* xs32 = (uint32_t*)xs_all[wave];
+  // word of token pair p (tokens 2p, 2p + 1) in column c: the 16-byte groups
+  // of 4 pairs are swizzled by bits 3-4 of the column, so the transposed
+  // writes of 8 columns x 4 pairs spread over the banks while a group of 8
+  // consecutive tokens stays one 16-byte read
+  auto xs_word = [](int c, int p) { return c * (XS / 2) + 4 * ((p >> 2) ^ ((c >> 3) & 3)) + (p & 3); };
   uint16_t* ys = ys_all[wave];
   const int hf = lane >> 5, col = lane & 31;
   // R1 rows as the A operand of xbar^T: lane (column, hf), K slot e' = rank 16m + 8hf + e'
@@ -533,19 +538,29 @@ __global__ __launch_bounds__(64 * kBwdXWaves) void bwd_x_kernel(BwdArgs a) {
   auto work = [&](long long j, const Blk& B) {
     __builtin_amdgcn_sched_barrier(0);
     const long long n0 = j * kTile;
-    // X slice -> LDS, transposed; rows past N and columns past the wave's end are zero
+    // X slice -> LDS, transposed; rows past N and columns past the wave's end
+    // are zero.  Lanes l and l ^ 8 hold tokens 2p and 2p + 1 of the same 8
+    // columns: they swap half their columns (DPP row_ror:8), and each writes
+    // 4 words holding both tokens of one column.
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = lane + 64 * i;
       const int tok = q / (WC / 8);
       const int cc = (q % (WC / 8)) * 8;
       const bool ok = n0 + tok < a.N && cc < ncol;
-      const u32x4 v = B.x[i];
+      const u32x4 v = ok ? B.x[i] : u32x4{0u, 0u, 0u, 0u};
+      const bool odd = (tok & 1) != 0;   // = (lane & 8) != 0
+      const uint32_t keep0 = odd ? v[2] : v[0], keep1 = odd ? v[3] : v[1];
+      const uint32_t send0 = odd ? v[0] : v[2], send1 = odd ? v[1] : v[3];
+      const uint32_t recv0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send0, 0x128, 0xf, 0xf, false);
+      const uint32_t recv1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send1, 0x128, 0xf, 0xf, false);
+      const uint32_t ev0 = odd ? recv0 : keep0, od0 = odd ? keep0 : recv0;   // even / odd token, 2 columns
+      const uint32_t ev1 = odd ? recv1 : keep1, od1 = odd ? keep1 : recv1;
+      const uint32_t w4[4] = {(ev0 & 0xffffu) | (od0 << 16), (ev0 >> 16) | (od0 & 0xffff0000u),
+                              (ev1 & 0xffffu) | (od1 << 16), (ev1 >> 16) | (od1 & 0xffff0000u)};
+      const int c0 = cc + (odd ? 4 : 0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w32 = v[e >> 1];
-        xs[(cc + e) * XS + tok] = ok ? (uint16_t)((e & 1) ? (w32 >> 16) : (w32 & 0xffff)) : (uint16_t)0;
-      }
+      for (int e = 0; e < 4; ++e) xs32[xs_word(c0 + e, tok >> 1)] = w4[e];
     }
     const bool tok_ok = n0 + col < a.N;
     bf16x8 zbh[R16], zbl[R16], zth[2], ztl[2];
@@ -586,7 +601,7 @@ __global__ __launch_bounds__(64 * kBwdXWaves) void bwd_x_kernel(BwdArgs a) {
       // R1bar^T partial: rows = ranks, column = h; K = the block's tokens
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const bf16x8 xb = __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + (u * kTile + col) * XS + 16 * m + 8 * hf));
+        const bf16x8 xb = __builtin_bit_cast(bf16x8, *(const u32x4*)(xs32 + xs_word(u * kTile + col, 8 * m + 4 * hf)));
         r1acc[u] = mfma_bf16(zth[m], xb, r1acc[u]);
         r1acc[u] = mfma_bf16(ztl[m], xb, r1acc[u]);
       }
