@@ -145,8 +145,42 @@ __global__ __launch_bounds__(256) void merge_vec_kernel(MergeArgs a) {
 // the wave (logit desc, index asc) and pop it from its lane.  The
 // full-softmax normaliser combines the lanes' shard values with a butterfly
 // (eq. (8)); the order of every sum is fixed.
+// (v2, i2) ahead of (v, i) in (logit desc, index asc)
+__device__ __forceinline__ bool ahead(float v2, int i2, float v, int i) { return v2 > v || (v2 == v && i2 < i); }
+
+// A <- the KMAX best of A and B, both ordered by (logit desc, index asc), in
+// that order: A[j] against B[KMAX-1-j] keeps the KMAX best as a bitonic
+// sequence, and a bitonic merge network orders it.
+template <int KMAX>
+__device__ __forceinline__ void bitonic_top(float (&V)[KMAX], int (&IX)[KMAX], const float (&BV)[KMAX],
+                                            const int (&BI)[KMAX]) {
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool b = ahead(BV[KMAX - 1 - j], BI[KMAX - 1 - j], V[j], IX[j]);
+    V[j] = b ? BV[KMAX - 1 - j] : V[j];
+    IX[j] = b ? BI[KMAX - 1 - j] : IX[j];
+  }
+#pragma unroll
+  for (int d = KMAX / 2; d >= 1; d >>= 1) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if ((j & d) == 0) {
+        const bool sw = ahead(V[j + d], IX[j + d], V[j], IX[j]);
+        const float v = V[j];
+        const int x = IX[j];
+        V[j] = sw ? V[j + d] : v;
+        IX[j] = sw ? IX[j + d] : x;
+        V[j + d] = sw ? v : V[j + d];
+        IX[j + d] = sw ? x : IX[j + d];
+      }
+    }
+  }
+}
+
 template <int KMAX, bool FULL>
 __global__ __launch_bounds__(256) void merge_wave_kernel(MergeArgs a) {
+  __shared__ float mw_lv[4][KMAX * kWave];   // per wave: the lanes' merged lists, [entry][lane]
+  __shared__ int mw_li[4][KMAX * kWave];
   const int lane = threadIdx.x & 63;
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= a.N) return;   // wave-uniform
@@ -158,21 +192,49 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(MergeArgs a) {
     IX[j] = 0x7fffffff;
   }
   float m = -__builtin_inff(), Z = 0.f;
-  for (int g = lane; g < a.G; g += kWave) {
-    const size_t base = ((size_t)g * a.N + n) * a.k;
+  // whole lists as 16-byte loads when every list is KMAX entries on a 16-byte boundary
+  const bool vec = a.k == KMAX && (KMAX % 4) == 0 && (((uintptr_t)a.cand_logit | (uintptr_t)a.cand_idx) & 15) == 0;
+  // lane l takes shards l, l + 64, ...: the first list as it is (each shard's
+  // list is ordered by (logit desc, index asc)), every further one by a
+  // bitonic top-KMAX merge
+  for (int it = 0; it * kWave < a.G; ++it) {
+    const int g = lane + it * kWave;
+    const bool gok = g < a.G;
+    const size_t base = ((size_t)(gok ? g : 0) * a.N + n) * a.k;
     const long long off = (long long)g * a.W;
-    // the shard's whole list first (its loads in flight together), then the inserts
     float cl[KMAX];
     int ci[KMAX];
+    if (vec) {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      cl[j] = j < a.k ? a.cand_logit[base + j] : -__builtin_inff();
-      ci[j] = j < a.k ? a.cand_idx[base + j] : 0x7fffffff;
+      for (int q = 0; q < KMAX / 4; ++q) {
+        const float4 x = ((const float4*)(a.cand_logit + base))[q];
+        const int4 y = ((const int4*)(a.cand_idx + base))[q];
+        cl[4 * q] = x.x, cl[4 * q + 1] = x.y, cl[4 * q + 2] = x.z, cl[4 * q + 3] = x.w;
+        ci[4 * q] = y.x, ci[4 * q + 1] = y.y, ci[4 * q + 2] = y.z, ci[4 * q + 3] = y.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        cl[j] = j < a.k ? a.cand_logit[base + j] : -__builtin_inff();
+        ci[j] = j < a.k ? a.cand_idx[base + j] : 0;
+      }
     }
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (cl[j] >= V[KMAX - 1]) ordered_insert<KMAX>(V, IX, cl[j], (int)(off + ci[j]));
-    if (FULL) {
+    for (int j = 0; j < KMAX; ++j) {
+      const bool real = gok && j < a.k;
+      cl[j] = real ? cl[j] : -__builtin_inff();
+      ci[j] = real ? (int)(off + ci[j]) : 0x7fffffff;
+    }
+    if (it == 0) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        V[j] = cl[j];
+        IX[j] = ci[j];
+      }
+    } else {
+      bitonic_top<KMAX>(V, IX, cl, ci);
+    }
+    if (FULL && gok) {
       const float l = a.shard_lse[(size_t)g * a.N + n];
       const float mn = fmaxf(m, l);
       Z = Z * __builtin_amdgcn_exp2f((m - mn) * kLog2e) + __builtin_amdgcn_exp2f((l - mn) * kLog2e);
@@ -189,36 +251,52 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(MergeArgs a) {
     for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
     lse = mm + __builtin_amdgcn_logf(z) * kLn2;
   }
-  // k rounds: the wave's best head, popped from the lane that holds it
+  // k rounds: the wave's best head, popped from the lane that holds it.  The
+  // best of each 16-lane row by DPP (quad swaps, then rotations by 4 and 8
+  // within the row), then of the four rows' results read into scalars.  The
+  // lane's list waits in LDS; only the lane that gave up its head reads the
+  // next entry.
+  float* lv = mw_lv[threadIdx.x >> 6];
+  int* li = mw_li[threadIdx.x >> 6];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    lv[j * kWave + lane] = V[j];
+    li[j * kWave + lane] = IX[j];
+  }
+  float hv = V[0];
+  int hx = IX[0], h = 0;
   float rv = -__builtin_inff();   // lane j keeps round j's logit and index
   int ri = 0x7fffffff;
+  auto take = [](float& v, int& i, float v2, int i2) {
+    const bool better = ahead(v2, i2, v, i);
+    v = better ? v2 : v;
+    i = better ? i2 : i;
+  };
+  for (int r = 0; r < a.k; ++r) {
+    float v = hv;
+    int i = hx;
+#define MORE_DPP_STEP(ctrl)                                                                                   \
+  take(v, i, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), ctrl, 0xf, 0xf, false)), \
+       __builtin_amdgcn_update_dpp(i, i, ctrl, 0xf, 0xf, false))
+    MORE_DPP_STEP(0xB1);    // quad_perm [1,0,3,2]
+    MORE_DPP_STEP(0x4E);    // quad_perm [2,3,0,1]
+    MORE_DPP_STEP(0x124);   // row_ror:4
+    MORE_DPP_STEP(0x128);   // row_ror:8
+#undef MORE_DPP_STEP
+    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-  for (int r = 0; r < KMAX; ++r) {
-    if (r < a.k) {
-      float v = V[0];
-      int i = IX[0];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float v2 = __shfl_xor(v, o);
-        const int i2 = __shfl_xor(i, o);
-        const bool better = v2 > v || (v2 == v && i2 < i);
-        v = better ? v2 : v;
-        i = better ? i2 : i;
-      }
-      if (lane == r) {
-        rv = v;
-        ri = i;
-      }
-      const bool pop = V[0] == v && IX[0] == i;
-#pragma unroll
-      for (int j = 0; j + 1 < KMAX; ++j) {
-        V[j] = pop ? V[j + 1] : V[j];
-        IX[j] = pop ? IX[j + 1] : IX[j];
-      }
-      if (pop) {
-        V[KMAX - 1] = -__builtin_inff();
-        IX[KMAX - 1] = 0x7fffffff;
-      }
+    for (int row = 1; row < 4; ++row)
+      take(bv, bi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * row)),
+           __builtin_amdgcn_readlane(i, 16 * row));
+    if (lane == r) {
+      rv = bv;
+      ri = bi;
+    }
+    if (hv == bv && hx == bi) {   // the lane that held it (several only for exhausted lists)
+      ++h;
+      hv = h < KMAX ? lv[h * kWave + lane] : -__builtin_inff();
+      hx = h < KMAX ? li[h * kWave + lane] : 0x7fffffff;
     }
   }
   // gates: round 0 holds the best logit
