@@ -145,38 +145,6 @@ __global__ __launch_bounds__(256) void merge_vec_kernel(MergeArgs a) {
 // the wave (logit desc, index asc) and pop it from its lane.  The
 // full-softmax normaliser combines the lanes' shard values with a butterfly
 // (eq. (8)); the order of every sum is fixed.
-// (v2, i2) ahead of (v, i) in (logit desc, index asc)
-__device__ __forceinline__ bool ahead(float v2, int i2, float v, int i) { return v2 > v || (v2 == v && i2 < i); }
-
-// A <- the KMAX best of A and B, both ordered by (logit desc, index asc), in
-// that order: A[j] against B[KMAX-1-j] keeps the KMAX best as a bitonic
-// sequence, and a bitonic merge network orders it.
-template <int KMAX>
-__device__ __forceinline__ void bitonic_top(float (&V)[KMAX], int (&IX)[KMAX], const float (&BV)[KMAX],
-                                            const int (&BI)[KMAX]) {
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    const bool b = ahead(BV[KMAX - 1 - j], BI[KMAX - 1 - j], V[j], IX[j]);
-    V[j] = b ? BV[KMAX - 1 - j] : V[j];
-    IX[j] = b ? BI[KMAX - 1 - j] : IX[j];
-  }
-#pragma unroll
-  for (int d = KMAX / 2; d >= 1; d >>= 1) {
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if ((j & d) == 0) {
-        const bool sw = ahead(V[j + d], IX[j + d], V[j], IX[j]);
-        const float v = V[j];
-        const int x = IX[j];
-        V[j] = sw ? V[j + d] : v;
-        IX[j] = sw ? IX[j + d] : x;
-        V[j + d] = sw ? v : V[j + d];
-        IX[j + d] = sw ? x : IX[j + d];
-      }
-    }
-  }
-}
-
 template <int KMAX, bool FULL>
 __global__ __launch_bounds__(256) void merge_wave_kernel(MergeArgs a) {
   __shared__ float mw_lv[4][KMAX * kWave];   // per wave: the lanes' merged lists, [entry][lane]

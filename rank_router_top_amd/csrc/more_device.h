@@ -276,10 +276,46 @@ __device__ __forceinline__ void ordered_insert(float (&V)[KMAX], int (&IX)[KMAX]
   }
 }
 
+// (v2, i2) ahead of (v, i) in (logit desc, index asc)
+__device__ __forceinline__ bool ahead(float v2, int i2, float v, int i) { return v2 > v || (v2 == v && i2 < i); }
+
+// A <- the KMAX best of A and B, both ordered by (logit desc, index asc), in
+// that order: A[j] against B[KMAX-1-j] keeps the KMAX best as a bitonic
+// sequence, and a bitonic merge network orders it.
+template <int KMAX>
+__device__ __forceinline__ void bitonic_top(float (&V)[KMAX], int (&IX)[KMAX], const float (&BV)[KMAX],
+                                            const int (&BI)[KMAX]) {
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool b = ahead(BV[KMAX - 1 - j], BI[KMAX - 1 - j], V[j], IX[j]);
+    V[j] = b ? BV[KMAX - 1 - j] : V[j];
+    IX[j] = b ? BI[KMAX - 1 - j] : IX[j];
+  }
+#pragma unroll
+  for (int d = KMAX / 2; d >= 1; d >>= 1) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if ((j & d) == 0) {
+        const bool sw = ahead(V[j + d], IX[j + d], V[j], IX[j]);
+        const float v = V[j];
+        const int x = IX[j];
+        V[j] = sw ? V[j + d] : v;
+        IX[j] = sw ? IX[j + d] : x;
+        V[j + d] = sw ? v : V[j + d];
+        IX[j + d] = sw ? x : IX[j + d];
+      }
+    }
+  }
+}
+
 // End of a token block: merge the two half-token logs of every token, order
 // by (logit desc, expert index asc), form the gates and store.  Must be called
 // with the whole wave active (the final compaction uses wave-wide votes).
-template <int KMAX, int CAP, bool FULL>
+// SPLIT: each half orders its own log and the halves' lists are merged with a
+// bitonic network (for few tokens per wave and long logs, as in the split-M
+// form); otherwise the low half orders both logs while the high half waits
+// (cheaper when the logs are short).
+template <int KMAX, int CAP, bool FULL, bool SPLIT = false>
 __device__ __forceinline__ void finish_tokens(SweepState<KMAX, CAP>& st, LogRef lg, int lane,
                                               bool hi_half, bool rowok, long long n,
                                               const int* __restrict__ perm, int k, int* out_idx,
@@ -287,7 +323,6 @@ __device__ __forceinline__ void finish_tokens(SweepState<KMAX, CAP>& st, LogRef 
   st.thr_p = partner_f32(st.L[KMAX - 1], hi_half);
   st.thr = fmaxf(st.L[KMAX - 1], st.thr_p);
   st.compact(lg, lane, perm, k);
-  const int cnt_p = (int)partner_u32((uint32_t)st.cnt, hi_half);
   float lse = 0.f;
   if (FULL) {
     // eq. (8) across the two halves: one running max and one normaliser per token
@@ -297,7 +332,6 @@ __device__ __forceinline__ void finish_tokens(SweepState<KMAX, CAP>& st, LogRef 
                      Zp * __builtin_amdgcn_exp2f((mp - mm) * kLog2e);
     lse = mm + __builtin_amdgcn_logf(Zt) * kLn2;
   }
-  if (hi_half || !rowok) return;
   float V[KMAX];
   int IX[KMAX];
 #pragma unroll
@@ -305,13 +339,33 @@ __device__ __forceinline__ void finish_tokens(SweepState<KMAX, CAP>& st, LogRef 
     V[j] = -__builtin_inff();
     IX[j] = 0x7fffffff;
   }
-  for (int c = 0; c < st.cnt; ++c) {
-    const float2 e = lg.base[c * kWave + lane];
-    ordered_insert<KMAX>(V, IX, e.x, perm[__float_as_int(e.y)]);
-  }
-  for (int c = 0; c < cnt_p; ++c) {
-    const float2 e = lg.base[c * kWave + lane + 32];
-    ordered_insert<KMAX>(V, IX, e.x, perm[__float_as_int(e.y)]);
+  if constexpr (SPLIT) {
+    // each half orders its own log, then the two halves' lists are merged
+    // (lane l and lane l ^ 32 end with the same KMAX best of the token)
+    for (int c = 0; c < st.cnt; ++c) {
+      const float2 e = lg.base[c * kWave + lane];
+      ordered_insert<KMAX>(V, IX, e.x, perm[__float_as_int(e.y)]);
+    }
+    float BV[KMAX];
+    int BI[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      BV[j] = partner_f32(V[j], hi_half);
+      BI[j] = (int)partner_u32((uint32_t)IX[j], hi_half);
+    }
+    bitonic_top<KMAX>(V, IX, BV, BI);
+    if (hi_half || !rowok) return;
+  } else {
+    const int cnt_p = (int)partner_u32((uint32_t)st.cnt, hi_half);
+    if (hi_half || !rowok) return;
+    for (int c = 0; c < st.cnt; ++c) {
+      const float2 e = lg.base[c * kWave + lane];
+      ordered_insert<KMAX>(V, IX, e.x, perm[__float_as_int(e.y)]);
+    }
+    for (int c = 0; c < cnt_p; ++c) {
+      const float2 e = lg.base[c * kWave + lane + 32];
+      ordered_insert<KMAX>(V, IX, e.x, perm[__float_as_int(e.y)]);
+    }
   }
   float w[KMAX];
   if (FULL) {

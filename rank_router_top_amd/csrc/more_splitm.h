@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void splitm_route_kernel(SplitmArgs sa) {
     if (t + 1 < t1) st.template tile<FULL>(accB, kTile * (t + 1) + 4 * hf, lg, lane, hi, a.perm, a.k);
   }
   const size_t so = (size_t)s * a.N;
-  finish_tokens<KMAX, CAP, FULL>(st, lg, lane, hi, rowok, n, a.perm, a.k, sa.cand_idx + so * a.k,
+  finish_tokens<KMAX, CAP, FULL, true>(st, lg, lane, hi, rowok, n, a.perm, a.k, sa.cand_idx + so * a.k,
                                  sa.cand_gate + so * a.k, sa.cand_logit + so * a.k,
                                  FULL ? sa.shard_lse + so : nullptr);
 }
