@@ -103,3 +103,35 @@ def test_dispatch_rejects_bad_arguments():
     with pytest.raises(R.MoreError) as e:
         R.dispatch_sort(t, 4096, workspace=small)
     assert e.value.code == R.MORE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("M", [300, 5000])
+def test_dispatch_out_of_range_entries_stay_in_bounds(M):
+    """Entries outside [0, M) have no defined place in the order (the header
+    says so), but the call must still write only inside its outputs: the
+    slots stay a permutation of 0 .. N k - 1.  With one pass (M <= 4096) the
+    offsets come from the digit counts (such entries count in the last
+    expert), so they stay a non-decreasing cover of 0 .. N k and every
+    in-range entry is still found under its own expert, in increasing slot
+    order."""
+    N, k = 3000, 4
+    idx = I.make_expert_sets(2, 65, N, M, k)
+    rng = np.random.default_rng(7)
+    bad = rng.random(idx.shape) < 0.05
+    idx = np.where(bad, np.where(rng.random(idx.shape) < 0.5, -3, M + 5), idx).astype(np.int32)
+    say(f"out-of-range entries: N={N} k={k} M={M} bad={int(bad.sum())}")
+    g = run_sort(idx, M)
+    flat = idx.reshape(-1)
+    ss, off = g["sorted_slot"], g["offsets"]
+    assert np.array_equal(np.sort(ss), np.arange(flat.size))
+    if M > 4096:
+        say("ok (several passes: slots only)")
+        return
+    assert off[0] == 0 and off[-1] == flat.size and np.all(np.diff(off) >= 0)
+    ok = (flat >= 0) & (flat < M)
+    for e in np.unique(flat[ok])[:50]:
+        run = ss[off[e]:off[e + 1]]
+        mine = np.nonzero(flat == e)[0]
+        assert np.all(np.isin(mine, run)), f"expert {e}: a slot is missing from its run"
+        assert np.all(np.diff(run[np.isin(run, mine)]) > 0)
+    say("ok")
