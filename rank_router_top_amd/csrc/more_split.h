@@ -389,41 +389,61 @@ __global__ __launch_bounds__(64 * WAVES) void route_kernel(RouteArgs ra) {
 #pragma unroll
     for (int m = 0; m < R16; ++m) acc = mfma_bf16(o.w[m], zl[m], acc);
   };
+  auto logits_hi = [&](const Ops& o, floatx16& acc) {
+#pragma unroll
+    for (int m = 0; m < R16; ++m) acc = mfma_bf16(o.w[m], zh[m], acc);
+  };
+  // the z-lo products of one tile alternating with the z-hi products of the
+  // next: each MFMA depends on the one issued two before it, not on the one
+  // just before (the per-tile order of the sums is that of logits())
+  auto logits2 = [&](const Ops& o1, floatx16& a1, const Ops& o2, floatx16& a2) {
+#pragma unroll
+    for (int m = 0; m < R16; ++m) {
+      a1 = mfma_bf16(o1.w[m], zl[m], a1);
+      a2 = mfma_bf16(o2.w[m], zh[m], a2);
+    }
+  };
 
   // Software pipeline over the expert tiles (pass lengths are multiples of
   // 4): tile t lives in slot t % 4 of two 4-slot register rings, its weight
   // operands (o) and its accumulator (ac).  At step t the VALU works on tile
-  // t while the MFMAs of tile t+1 run; the weight operands of tile t+1 were
-  // requested at step t-4 (three newer requests may still be in flight), and
-  // its accumulator was loaded with its bias (LDS) at step t-3, right after
-  // tile t-3 left that slot, so the MFMAs accumulate in place.  Every pass
-  // starts at tile 0, so near its end both rings are refilled with tiles
-  // 0..3 of the next pass (seed pass -> sweep -> next block's seed pass); the
-  // last step's MFMAs run on the next pass's tile 0 and are discarded (every
-  // step has the same loads and MFMAs, which keeps the wait counts static).
+  // t while the MFMAs run that finish tile t+1 (its z-lo products) and start
+  // tile t+2 (its z-hi products), alternating, so no MFMA waits for the
+  // result of the one issued just before it.  The weight operands of tile
+  // t+2 were requested at step t-3 (the newer requests of two steps may
+  // still be in flight), and its accumulator was loaded with its bias (LDS)
+  // at step t-1, right after tile t-2 left that slot, so the MFMAs
+  // accumulate in place.  Every pass starts at tile 0, so near its end both
+  // rings are refilled with tiles 0..3 of the next pass (seed pass -> sweep
+  // -> next block's seed pass); the last two steps' MFMAs on the next pass's
+  // tiles 0 and 1 are discarded and redone when it starts (every step has
+  // the same loads and MFMAs, which keeps the wait counts static; the next
+  // block's z replaces the current one between the passes).
   Ops o[4];
   floatx16 ac[4];
   load_z(0);
 #pragma unroll
   for (int u = 0; u < 4; ++u) load_ops(u, o[u]);
-  ac[1] = bias(1);
   ac[2] = bias(2);
   // One pass over tiles 0..len-1.  scan(acc, t) is the branch-free work on
-  // tile t; it is interleaved with the MFMAs of tile t+1 (one MFMA, then a
-  // few VALU instructions, ...), so the wave keeps issuing while each MFMA of
-  // the dependent chain runs.  log(acc, t, s) is the rare branchy part.
+  // tile t; it is interleaved with the step's MFMAs (one MFMA, then a few
+  // VALU instructions, ...), so the wave keeps issuing while they run.
+  // log(acc, t, s) is the rare branchy part.
   auto sweep = [&](int len, auto&& scan, auto&& log) {
     auto wrap = [&](int t) { return t >= len ? t - len : t; };   // t < 2 len
-    ac[0] = bias(0);   // the previous pass's last step ran its discarded MFMAs on this slot
+    // the previous pass's last two steps ran their discarded MFMAs on slots 0 and 1
+    ac[0] = bias(0);
+    ac[1] = bias(1);
     logits(o[0], ac[0]);
     load_ops(wrap(4), o[0]);
+    logits_hi(o[1], ac[1]);
     for (int t0 = 0; t0 < len; t0 += 4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = t0 + u;
-        const bool last = t == len - 1;   // then tile t+1 is the next pass's tile 0 (discarded)
+        const bool last = t == len - 1;   // reload tile 0 of the next pass into its slot
         ac[(u + 3) & 3] = bias(wrap(t + 3));   // the slot of tile t-1, done with at step t-1
-        logits(o[(u + 1) & 3], ac[(u + 1) & 3]);
+        logits2(o[(u + 1) & 3], ac[(u + 1) & 3], o[(u + 2) & 3], ac[(u + 2) & 3]);
         load_ops(last ? 0 : wrap(t + 5), o[(u + 1) & 3]);
         const auto sc = scan(ac[u], t);
 #pragma unroll
