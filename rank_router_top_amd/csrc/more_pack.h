@@ -42,7 +42,7 @@ struct PackArgs {
   float* biasp;       // [NT][2][16] fp32, accumulator layout (fp32 kernels)
   uint32_t* biasq;    // [NT][64] bf16 pairs (hi, lo) as an MFMA A operand (bf16 kernels)
   int* perm;          // [Mpad]: read (with a bias: sorted beforehand) or written (without)
-  int sorted;         // 1: perm was written by order_count_kernel (bias-descending order)
+  int sorted;         // 1: perm was written by the order kernels (bias-descending order)
   int* status;        // the routing calls' stall word: cleared (null: left alone)
   int* seed;          // seed-pass length of the LDS-ring sweep (tiles), written (null: left alone)
   int seed_tiles;
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(1024) void pack_kernel(PackArgs a) {
   }
   if ((int)blockIdx.x < a.rank_blocks) {
     // ---- sweep position pos holds expert j = perm[pos] (sorted by
-    // order_count_kernel with a bias; index order otherwise); padding last
+    // order kernels with a bias; index order otherwise); padding last
     const int jl = tid & 63, slice = tid >> 6;   // 64 positions x 16 slices
     // Mpad is a multiple of 64: every position of the block is real
     const int pos = blockIdx.x * 64 + jl;

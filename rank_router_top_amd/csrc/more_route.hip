@@ -43,7 +43,7 @@ size_t log_bytes(int kmax) { return (size_t)(2 * kmax + 8) * kWave * sizeof(floa
 
 struct Layout {
   int NT, Mpad, r16, rb, ks1, ks2, ksq, epl, esize;
-  size_t off_status, off_r1p, off_r2p, off_bias, off_biasq, off_perm, off_r1q, off_seed, total;
+  size_t off_status, off_r1p, off_r2p, off_bias, off_biasq, off_perm, off_okeys, off_r1q, off_seed, total;
 };
 
 // Workspace layout of one call.  All offsets are 256-byte aligned.
@@ -92,6 +92,10 @@ bool make_layout(int fullrank, more_dtype dt, int64_t h, int64_t r, int64_t M, L
   off += align_up((size_t)((L->NT + 3) / 4 * 4) * kWave * sizeof(uint32_t));
   L->off_perm = off;
   off += align_up((size_t)L->Mpad * sizeof(int));
+  // sorted chunks of bias keys (the bias-descending order is built from them)
+  L->off_okeys = off;
+  if (M <= kOrderMaxM)
+    off += align_up((size_t)((M + kOrderChunk - 1) / kOrderChunk) * kOrderChunk * sizeof(uint32_t));
   L->off_r1q = off;
   off += align_up((size_t)L->ksq * L->r16 * 1024);
   // weight statistics of the sweep kernel's error bound and seed pass
@@ -467,8 +471,12 @@ more_status launch_pack(more_dtype dt, int fullrank, const void* A, const void* 
     o.bias = bias;
     o.M = (int)M;
     o.Mpad = L.Mpad;
+    o.keys = (uint32_t*)(ws + L.off_okeys);
     o.perm = p.perm;
-    hipLaunchKernelGGL(order_count_kernel, dim3((L.Mpad + 15) / 16), dim3(256), 0, stream, o);
+    hipLaunchKernelGGL(order_sort_kernel, dim3((unsigned)((M + kOrderChunk - 1) / kOrderChunk)), dim3(kOrderSortThreads),
+                       0, stream, o);
+    hipLaunchKernelGGL(order_rank_kernel, dim3((unsigned)((L.Mpad + kOrderThreads - 1) / kOrderThreads)),
+                       dim3(kOrderThreads), 0, stream, o);
     if (hipGetLastError() != hipSuccess) return MORE_ERR_HIP;
   }
   p.sorted = ordered ? 1 : 0;

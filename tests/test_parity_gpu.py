@@ -120,6 +120,8 @@ def test_fullrank_tiny_fp32(oracle_lib):
     (130, 256, 48, 1000, 32, "bf16"),  # k = 32 (largest list), r = 48 padded to 64
     (97, 96, 16, 257, 16, "f32"),      # fp32 path, k = 16
     (64, 64, 128, 64, 32, "f32"),      # fp32, r = 128, k = M/2
+    (2048 + 40, 256, 32, 4096 + 700, 8, "bf16"),   # two-kernel path, 3 chunks of the bias order, last one ragged
+    (120, 128, 16, 16384 - 3, 8, "bf16"),          # largest M with the bias-descending order (8 chunks)
 ])
 def test_edge_shapes(oracle_lib, N, h, r, M, k, dt):
     rng = np.random.default_rng(N * 7 + M)
@@ -180,6 +182,22 @@ def test_exact_ties_lower_index_wins(oracle_lib):
             # ordered index lists must agree wherever the oracle's distinct values
             # are separated by more than the GPU's rounding
             assert np.array_equal(g["idx"], o["idx"]), "tie rule violated"
+
+
+def test_bias_ties_across_order_chunks(oracle_lib):
+    """Biases on a coarse grid (many exact ties, -0 and +0 among them) across
+    the 2048-expert chunks the sweep order is built from: the order must still
+    be a permutation, so the result matches the oracle."""
+    rng = np.random.default_rng(11)
+    N, h, r, M, k = 2048 + 17, 128, 32, 6000, 8
+    X = rng.standard_normal((N, h))
+    X /= np.sqrt(np.mean(X * X, axis=1, keepdims=True))
+    R1 = rng.standard_normal((h, r)) / math.sqrt(h)
+    R2 = rng.standard_normal((r, M)) / math.sqrt(r)
+    b = (np.round(rng.standard_normal(M) * 2) / 4).astype(np.float32)
+    b[::7] = -0.0
+    conv = lambda a: I.f32_to_bf16_bits(a.astype(np.float32))
+    check_lowrank(oracle_lib, conv(X), conv(R1), conv(R2), b, k, 0, "bias-ties-6000")
 
 
 def test_all_equal_logits(oracle_lib):
