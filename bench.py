@@ -108,6 +108,12 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, "
                          "both with --calib-copy) into profiles/traffic_<workload>.json and exit")
+    ap.add_argument("--counters-from", nargs="+", metavar="PMC_DIR",
+                    help="turn rocprofv3 --pmc runs of this script with SQ counters (SQ_BUSY_CYCLES, "
+                         "SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_*) into profiles/counters_<workload>.json and exit")
+    ap.add_argument("--whole-calls", type=int, default=11,
+                    help="with --counters-from: routing-kernel dispatches of whole calls at the start of "
+                         "each run (warmup + steps), left out: they include the ready-word polls")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of 256 MiB three times (byte-counter calibration "
                          "for rocprofv3 --pmc runs)")
@@ -191,6 +197,65 @@ def write_traffic(args):
         json.dump(res, f, indent=1)
         f.write("\n")
     print(json.dumps(res))
+    return 0
+
+
+N_SIMD, N_SE = 1024, 32   # MI355X: 256 CUs x 4 SIMDs; 8 XCDs x 4 shader engines
+
+
+def write_counters(args):
+    """Per-dispatch means of the SQ counters of the two routing-call kernels
+    (the routing kernel over its packed-weight dispatches only) and what they
+    give: the MFMA pipe's busy fraction (busy cycles per SIMD over the SQ's busy
+    cycles per shader engine, one clock domain) and the instruction mix."""
+    import csv
+    import glob
+    from rank_router_top_amd import configs as CF
+    cfg = CF.ALL[args.workload]
+    sums = {}
+    for d in args.counters_from:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for fn in files:
+            per = {}
+            with open(fn) as f:
+                for row in csv.DictReader(f):
+                    kn = next((k for k in ROUTER_KERNELS if k in row["Kernel_Name"]), None)
+                    if kn:
+                        key = (kn, row["Counter_Name"], int(row["Dispatch_Id"]))
+                        per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+            route_ids = sorted({di for (kn, _, di) in per if kn == ROUTER_KERNELS[1]})
+            whole = set(route_ids[:args.whole_calls])
+            for (kn, c, di), v in per.items():
+                if kn == ROUTER_KERNELS[1] and di in whole:
+                    continue
+                sums.setdefault((kn, c), []).append(v)
+    kernels = {kn: {c: sum(v) / len(v) for (k2, c), v in sums.items() if k2 == kn} for kn in ROUTER_KERNELS}
+    derived = {}
+    for kn, cs in kernels.items():
+        dd = {}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in cs and "SQ_BUSY_CYCLES" in cs:
+            dd["mfma_busy_frac"] = (cs["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD) / (cs["SQ_BUSY_CYCLES"] / N_SE)
+        if "SQ_ACTIVE_INST_ANY" in cs and "SQ_WAVE_CYCLES" in cs:
+            dd["wave_issue_frac"] = cs["SQ_ACTIVE_INST_ANY"] / cs["SQ_WAVE_CYCLES"]
+        if "SQ_WAIT_ANY" in cs and "SQ_WAVE_CYCLES" in cs:
+            dd["wave_wait_frac"] = cs["SQ_WAIT_ANY"] / cs["SQ_WAVE_CYCLES"]
+        derived[kn] = dd
+    rk = kernels[ROUTER_KERNELS[1]]
+    if cfg.name == "headline" and "SQ_INSTS_VALU" in rk:
+        visits = (cfg.N // 32) * (24 + (cfg.M + 31) // 32)   # blocks x (seed + sweep) tile visits
+        derived[ROUTER_KERNELS[1]]["per_wave_tile"] = {
+            c.replace("SQ_INSTS_", "").lower(): rk[c] / visits for c in
+            ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_BRANCH") if c in rk}
+        derived[ROUTER_KERNELS[1]]["per_wave_tile"]["valu"] -= derived[ROUTER_KERNELS[1]]["per_wave_tile"].get("mfma", 0)
+    res = {"workload": cfg.name, "source_hash": source_hash(), "n_simd": N_SIMD, "n_se": N_SE,
+           "kernels": kernels, "derived": derived}
+    path = os.path.join(ROOT, "profiles", f"counters_{cfg.name}.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(derived))
     return 0
 
 
@@ -345,6 +410,8 @@ def main():
     args = parse()
     if args.traffic_from:
         return write_traffic(args)
+    if args.counters_from:
+        return write_counters(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this router benchmark runs on exactly one GPU; "
                                    "multi-GPU runs are not supported (token sharding would need no "
@@ -430,6 +497,15 @@ def main():
             tr = json.load(f)
         if tr.get("source_hash") == source_hash():
             traffic = tr.get("bytes_per_launch")
+    # MFMA busy fraction and issue / wait fractions of the two kernels from the
+    # committed SQ counter runs, under the same condition
+    counters = None
+    cpath = os.path.join(ROOT, "profiles", f"counters_{cfg.name}.json")
+    if os.path.exists(cpath):
+        with open(cpath) as f:
+            cr = json.load(f)
+        if cr.get("source_hash") == source_hash():
+            counters = {"source": os.path.relpath(cpath, ROOT), **cr.get("derived", {})}
 
     result = {
         "metric": "routed tokens/sec & % roofline, N=262144 h=2048 M=4096 r=32 k=8, 1 GPU",
@@ -455,7 +531,7 @@ def main():
                      "kernel_ms_p10": k_p10, "kernel_ms_p90": k_p90,
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "mfma_tflops": cfg.flops() / (k_mean * 1e-3) / 1e12,
-                     "pack_kernel_ms": p_mean},
+                     "pack_kernel_ms": p_mean, "counters": counters},
         "context": CONTEXT,
     }
 
