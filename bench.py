@@ -64,13 +64,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 # the kernels one routing call of the headline workload runs (rocprofv3 names)
-ROUTER_KERNELS = ("more::proj_kernel<2, 16, false, 4>", "more::route_kernel<8, false, 2, 8, false>")
+ROUTER_KERNELS = ("more::proj_kernel<2, 16, false, 3>", "more::route_kernel<8, false, 2, 8, false>")
 KERNEL_NAME = " + ".join(ROUTER_KERNELS)
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published (no sparsity)
 # v_exp_f32 rate: 256 CUs x 4 SIMDs x 16 lanes per cycle at half rate (one wave64
 # exp per 8 cycles, measured against v_fma_f32 at one per 4), 2.4 GHz
 EXP_PEAK_PER_S = 256 * 4 * 16 / 2 * 2.4e9
-BALANCE_KERNELS = ("more::proj_kernel<2, 16, false, 4>", "more::route_kernel<8, false, 2, 8, true>",
+BALANCE_KERNELS = ("more::proj_kernel<2, 16, false, 3>", "more::route_kernel<8, false, 2, 8, true>",
                    "more::psum_kernel<2, 8, 8>", "more::count_kernel", "more::colsum_kernel",
                    "more::stats_kernel")
 CONTEXT = {

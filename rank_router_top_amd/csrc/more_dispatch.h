@@ -59,7 +59,7 @@ pc_fn pick_pc(bool full, int kmax, int r16, bool tail);
 // Two-kernel form (projection + routing): bf16, k <= 8, r <= 64, M <= 65535.
 typedef void (*proj_fn)(ProjArgs);
 typedef void (*route_fn)(RouteArgs);
-constexpr int kProjWaves = 4;    // projection: one streaming wave per SIMD (+1 writer), one workgroup per CU
+constexpr int kProjWaves = 3;    // projection: three streaming waves + the writer, one per SIMD; one workgroup per CU
 constexpr int kRouteWaves = 8;   // routing: eight waves, one workgroup per CU
 // Projection ring depth (X loads in flight per wave): 16, or 8 at r = 64,
 // where the packed down-projection takes more of the LDS.

@@ -169,8 +169,8 @@ def test_balance_workspace_bytes():
     assert R.balance_workspace_bytes(bf, 10, 2048, 128, 4096, 8) == 0
     assert R.balance_workspace_bytes(bf, 10, 4608, 16, 4096, 8) > 0       # R1 resident in LDS
     assert R.balance_workspace_bytes(bf, 10, 4864, 16, 4096, 8) == 0
-    assert R.balance_workspace_bytes(bf, 10, 768, 64, 4096, 8) > 0
-    assert R.balance_workspace_bytes(bf, 10, 1024, 64, 4096, 8) == 0
+    assert R.balance_workspace_bytes(bf, 10, 1024, 64, 4096, 8) > 0       # R1 (128 KiB) + 3 z slots fit
+    assert R.balance_workspace_bytes(bf, 10, 1056, 64, 4096, 8) == 0
     assert R.balance_workspace_bytes(bf, 10, 2048, 32, 4096, 9) == 0
 
 

@@ -134,7 +134,7 @@ def test_balance_configs(oracle_lib, cfg, n, gate):
     (64, 128, 16, 8, 8, True),         # k = M: every expert selected by every token
     (300, 128, 48, 200, 1, True),      # r = 48 (three 16-rank blocks, padded to four), k = 1
     (96, 256, 64, 5888, 8, True),      # the largest M of the envelope at k = 8
-    (200, 768, 64, 4096, 8, True),     # r = 64 at the largest h of the envelope
+    (200, 1024, 64, 4096, 8, True),    # r = 64 at the largest h of the envelope
     (96, 256, 32, 14720, 4, True),     # the largest M of the envelope at k = 4
 ])
 def test_balance_edge_shapes(oracle_lib, N, h, r, M, k, bias):

@@ -122,6 +122,7 @@ def test_fullrank_tiny_fp32(oracle_lib):
     (64, 64, 128, 64, 32, "f32"),      # fp32, r = 128, k = M/2
     (2048 + 40, 256, 32, 4096 + 700, 8, "bf16"),   # two-kernel path, 3 chunks of the bias order, last one ragged
     (120, 128, 16, 16384 - 3, 8, "bf16"),          # largest M with the bias-descending order (8 chunks)
+    (2048 + 50, 1024, 64, 4096, 8, "bf16"),        # two-kernel path at r = 64, the largest h whose R1 fits its LDS
 ])
 def test_edge_shapes(oracle_lib, N, h, r, M, k, dt):
     rng = np.random.default_rng(N * 7 + M)
