@@ -508,7 +508,7 @@ def main():
             counters = {"source": os.path.relpath(cpath, ROOT), **cr.get("derived", {})}
 
     result = {
-        "metric": "routed tokens/sec & % roofline, N=262144 h=2048 M=4096 r=32 k=8, 1 GPU",
+        "metric": f"routed tokens/sec & % roofline, N={cfg.N} h={cfg.h} M={cfg.M} r={cfg.r} k={cfg.k}, 1 GPU",
         "value": cfg.N / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
