@@ -274,7 +274,7 @@ more_status launch_splitm(const LowRankArgs& a, const Layout& L, const SplitmPla
   sa.cand_gate = (float*)(scratch + P.off_cg);
   sa.shard_lse = full ? (float*)(scratch + P.off_lse) : nullptr;
   splitm_fn rf = full ? pick_splitm_full(kmax, L.r16) : pick_splitm_topk(kmax, L.r16);
-  const size_t lds = 4 * log_bytes(kmax);
+  const size_t lds = splitm_lds_bytes(kmax);
   if (hipFuncSetAttribute((const void*)rf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return MORE_ERR_HIP;
   const int rw = P.NB * P.S;
@@ -604,7 +604,7 @@ more_status route_packed(more_dtype dt, const void* X, int64_t N, int64_t h, int
   SplitmPlan sp;
   const size_t zbytes = z_scratch_bytes(dt, L, N);
   const bool splitm = path_allowed(kPathSplitM) && splitm_plan(dt, L, N, h, k, &sp) &&
-                      workspace_bytes >= L.total + sp.bytes && 4 * log_bytes(kmax) <= (size_t)kLdsBytes;
+                      workspace_bytes >= L.total + sp.bytes && splitm_lds_bytes(kmax) <= (size_t)kLdsBytes;
   if (!splitm && zbytes > 0 && workspace_bytes >= L.total + zbytes) {
     if (path_allowed(kPathSplit) && split_fits(kmax, L, h, false))
       return launch_split(a, L, h, kmax, full, full, false, ws, (hipStream_t)stream, side);

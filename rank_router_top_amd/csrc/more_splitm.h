@@ -23,6 +23,7 @@
 #pragma once
 #include "more_device.h"
 #include "more_lowrank.h"
+#include "more_twopass.h"
 
 namespace more {
 
@@ -100,6 +101,28 @@ __global__ __launch_bounds__(64) void splitm_proj_kernel(SplitmProjArgs a) {
   for (int q = 0; q < RB; ++q)
 #pragma unroll
     for (int v = 0; v < 16; ++v) dst[((size_t)q * 16 + v) * kWave + lane] = z[q][v];
+}
+
+// The routing kernel's selection for a shard: the two-pass group log of
+// more_twopass.h where its per-wave LDS (log of KMAX + 2 groups per lane,
+// result block) fits four waves in a workgroup, the running top-k above.
+template <int KMAX>
+struct SplitmTwoPass {
+  static constexpr bool value = KMAX <= 16;
+  static constexpr int kCapG = KMAX + 2;
+  static constexpr int kValBytes = kCapG * kWave * 16;
+  static constexpr int kPosBytes = kCapG * kWave * 4;
+  static constexpr int kWaveBytes = kValBytes + kPosBytes + TpStage<KMAX>::kWords * 4;
+};
+
+// Dynamic LDS of splitm_route_kernel (four waves).
+inline size_t splitm_lds_bytes(int kmax) {
+  switch (kmax) {
+    case 4: return 4 * (size_t)SplitmTwoPass<4>::kWaveBytes;
+    case 8: return 4 * (size_t)SplitmTwoPass<8>::kWaveBytes;
+    case 16: return 4 * (size_t)SplitmTwoPass<16>::kWaveBytes;
+    default: return 4 * (size_t)(2 * kmax + 8) * kWave * sizeof(float2);   // running top-k log
+  }
 }
 
 struct SplitmArgs {
@@ -187,26 +210,68 @@ __global__ __launch_bounds__(256) void splitm_route_kernel(SplitmArgs sa) {
     for (int m = 0; m < R16; ++m) acc = mfma_bf16(o.w[m], zl[m], acc);
     return acc;
   };
-  SweepState<KMAX, CAP> st;
-  st.init(a.k);
-  // two tiles in flight, as in lowrank_kernel
-  Ops o0, o1;
-  load_ops(t0, o0);
-  load_ops(t0 + 1, o1);
-  floatx16 accA = logits(o0);
-  load_ops(t0 + 2, o0);
-  for (int t = t0; t < t1; t += 2) {
-    floatx16 accB = logits(o1);
-    load_ops(t + 3, o1);
-    st.template tile<FULL>(accA, kTile * t + 4 * hf, lg, lane, hi, a.perm, a.k);
-    accA = logits(o0);   // beyond the shard's last tile: unused
-    load_ops(t + 4, o0);
-    if (t + 1 < t1) st.template tile<FULL>(accB, kTile * (t + 1) + 4 * hf, lg, lane, hi, a.perm, a.k);
-  }
+  // the shard's tiles with two in flight, as in lowrank_kernel; on_tile(acc, t)
+  auto sweep = [&](auto&& on_tile) {
+    Ops o0, o1;
+    load_ops(t0, o0);
+    load_ops(t0 + 1, o1);
+    floatx16 accA = logits(o0);
+    load_ops(t0 + 2, o0);
+    for (int t = t0; t < t1; t += 2) {
+      floatx16 accB = logits(o1);
+      load_ops(t + 3, o1);
+      on_tile(accA, t);
+      accA = logits(o0);   // beyond the shard's last tile: unused
+      load_ops(t + 4, o0);
+      if (t + 1 < t1) on_tile(accB, t + 1);
+    }
+  };
   const size_t so = (size_t)s * a.N;
-  finish_tokens<KMAX, CAP, FULL, true>(st, lg, lane, hi, rowok, n, a.perm, a.k, sa.cand_idx + so * a.k,
-                                 sa.cand_gate + so * a.k, sa.cand_logit + so * a.k,
-                                 FULL ? sa.shard_lse + so : nullptr);
+  if constexpr (SplitmTwoPass<KMAX>::value) {
+    // Two passes over the shard (more_twopass.h): the 4-logit group maxima give
+    // a lower bound of each token's k-th logit, the second pass logs the 4-logit
+    // groups that reach it (and accumulates eq. 8), and one ordered finish
+    // forms the shard's k best.  Wave-wide work per tile stays small: a
+    // running top-k would insert a logit whenever any of the 64 lanes holds
+    // one above its own k-th.
+    typedef SplitmTwoPass<KMAX> TP;
+    typedef TpStage<KMAX> SG;
+    char* wl = (char*)smem_log + (size_t)wave * TP::kWaveBytes;
+    const GroupLog glog{(lds_f4*)wl, (lds_i32*)(wl + TP::kValBytes)};
+    lds_f32* stg = (lds_f32*)(wl + TP::kValBytes + TP::kPosBytes);
+    TwoPassState<KMAX> st;
+    st.init(a.k);
+    sweep([&](const floatx16& acc, int) { tp_pass1_groups<KMAX>(st, acc); });
+    tp_threshold<KMAX>(st, hi, a.k);
+    sweep([&](const floatx16& acc, int t) {
+      const floatx4 g = tp_pass2_scan<KMAX, false>(st, acc, false);
+      if (FULL) tp_lse_tile<KMAX>(st, acc, g);
+      tp_pass2_groups<KMAX, TP::kCapG>(st, acc, g, kTile * t + 4 * hf, glog, lane, a.perm, a.k);
+    });
+    tp_finish_groups<KMAX, false, FULL>(st, glog, lane, hi, a.perm, a.k, true, stg);
+    lds_drain();
+    // the block's rows of the stage (token t's k entries at t k .. t k + k - 1)
+    // -> the shard's candidate lists; rows past N are dropped
+    const long long n0 = (long long)b * kTile;
+    const int rows = a.N - n0 < kTile ? (int)(a.N - n0) : kTile;
+    const int words = rows * a.k;
+    int* ci = sa.cand_idx + (so + n0) * a.k;
+    float* cl = sa.cand_logit + (so + n0) * a.k;
+    for (int c = lane; c < words; c += kWave) {
+      ci[c] = __float_as_int(stg[SG::kIdx + c]);
+      cl[c] = stg[SG::kLogit + c];
+    }
+    if (FULL && lane < rows) sa.shard_lse[so + n0 + lane] = stg[SG::kLse + lane];
+  } else {
+    SweepState<KMAX, CAP> st;
+    st.init(a.k);
+    sweep([&](const floatx16& acc, int t) {
+      st.template tile<FULL>(acc, kTile * t + 4 * hf, lg, lane, hi, a.perm, a.k);
+    });
+    finish_tokens<KMAX, CAP, FULL, true>(st, lg, lane, hi, rowok, n, a.perm, a.k, sa.cand_idx + so * a.k,
+                                   sa.cand_gate + so * a.k, sa.cand_logit + so * a.k,
+                                   FULL ? sa.shard_lse + so : nullptr);
+  }
 }
 
 }  // namespace more

@@ -88,6 +88,18 @@ __device__ __forceinline__ void tp_pass1_tile(TwoPassState<KMAX>& st, const floa
   med3_insert<KMAX>(st.L, tmax);
 }
 
+// Pass 1 with the four group maxima of the tile instead of its maximum: the
+// groups are disjoint, so their maxima are distinct logits of the token and
+// the k-th largest of them is still a lower bound of its k-th logit, a much
+// closer one when a lane sees few tiles (the expert shards of the split-M
+// form).  16 more VALU per tile and list length.
+template <int KMAX>
+__device__ __forceinline__ void tp_pass1_groups(TwoPassState<KMAX>& st, const floatx16& acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    med3_insert<KMAX>(st.L, fmaxf(fmaxf(acc[4 * q], acc[4 * q + 1]), fmaxf(acc[4 * q + 2], acc[4 * q + 3])));
+}
+
 // End of pass 1: token threshold = k-th largest of both halves' tile maxima
 // (identical on the two lanes of a token).
 template <int KMAX>
