@@ -461,8 +461,20 @@ __global__ __launch_bounds__(64 * WAVES) void route_kernel(RouteArgs ra) {
   TwoPassState<KMAX> st;
   for (int jj = 0; jj < nj; ++jj) {
     st.init(a.k);
+    // pass 1: with a bias, a seed over the first tiles of the bias-descending
+    // order bounded by the 4-logit group maxima (closer than the tile maxima,
+    // so fewer groups reach the bound in the sweep); without one, a full pass
+    // on the tile maxima (group maxima over every tile cost more than they
+    // save there)
     sweep(
-        P, [&](const floatx16& acc, int) { tp_pass1_tile<KMAX, false>(st, acc); return 0; },
+        P,
+        [&](const floatx16& acc, int) {
+          if (has_bias)   // workgroup-uniform
+            tp_pass1_groups<KMAX>(st, acc);
+          else
+            tp_pass1_tile<KMAX, false>(st, acc);
+          return 0;
+        },
         [&](const floatx16&, int, int) {});
     tp_threshold<KMAX>(st, hi, a.k);
     sweep(
