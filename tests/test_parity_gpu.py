@@ -149,6 +149,8 @@ def test_edge_shapes(oracle_lib, N, h, r, M, k, dt):
     (2048, 2048, 32, 4096, 8),
     (300, 1024, 128, 20000, 4),
     (77, 256, 16, 32 * 260 + 1, 8),
+    (77, 256, 16, 32 * 260 + 1, 16),     # two-pass shards at k = 16, the last shard with one real expert
+    (100, 512, 32, 8192 + 5, 12),        # k below the 16-wide lists (their +inf pads)
 ])
 def test_splitm_shapes(oracle_lib, route_paths, N, h, r, M, k):
     route_paths("splitm")
