@@ -478,13 +478,17 @@ __device__ __forceinline__ void tp_finish_groups(const TwoPassState<KMAX>& st, G
     med3_insert<KMAX>(T, j >= KMAX - k ? p : kLowest);
   }
   const float vk = T[KMAX - 1];
-  // 2. without exact ties among the selected logits and at the k-th place,
-  //    a logit's rank is the number of selected logits above it: each half
-  //    writes the expert index of its own selected logits straight into the
-  //    token's result row.  Otherwise (rare) an exact merge orders them.
+  // 2. the selected logits (>= vk) of each half go, with their sweep
+  //    positions, straight into the token's result row: the low half fills
+  //    it from slot 0 up, the high half from slot k-1 down.  Without exact
+  //    ties among them and at the k-th place there are exactly k, so they
+  //    fill the row, and the low half then orders the k entries by their rank
+  //    in T (the number of larger selected logits).  Otherwise (rare) an
+  //    exact merge over both logs rewrites the row.
   const int tok = lane & 31;
   const int o = tok * k;
-  // rank-writes (valid only without ties; the slow path rewrites every rank)
+  const int s0 = hi_half ? o + k - 1 : o;
+  const int sd = hi_half ? -1 : 1;
   int nge = 0;
 #pragma unroll 2
   for (int c = 0; c < st.cnt; ++c) {
@@ -493,11 +497,12 @@ __device__ __forceinline__ void tp_finish_groups(const TwoPassState<KMAX>& st, G
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (v[e] >= vk) {
+        if (nge < k) {   // more only with ties: the slots stay in the token's row
+          const int sl = s0 + sd * nge;
+          stg[S::kLogit + sl] = v[e];
+          stg[S::kIdx + sl] = __int_as_float(p + e);
+        }
         ++nge;
-        int r = -(KMAX - k);   // the +inf pads count as larger
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) r += T[j] > v[e] ? 1 : 0;
-        if (r < k) stg[S::kIdx + o + r] = __int_as_float((int)perm[p + e]);
       }
     }
   }
@@ -507,6 +512,22 @@ __device__ __forceinline__ void tp_finish_groups(const TwoPassState<KMAX>& st, G
   float V[KMAX];
   if (!any_lane(tie)) {
     if (hi_half) return;
+    float sv[KMAX];
+    int sp[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      sv[j] = j < k ? stg[S::kLogit + o + j] : kLowest;
+      sp[j] = j < k ? __float_as_int(stg[S::kIdx + o + j]) : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k) {
+        int r = -(KMAX - k);   // the +inf pads count as larger
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) r += T[i] > sv[j] ? 1 : 0;
+        stg[S::kIdx + o + r] = __int_as_float((int)perm[sp[j]]);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) V[j] = T[(j + KMAX - k) < KMAX ? (j + KMAX - k) : KMAX - 1];
   } else {
